@@ -1,0 +1,796 @@
+// Staged decode on gfx950: routed experts read through the slot table from a
+// fixed slot pool, int4 group-64 dequantised in registers, gate and up fused
+// in one pass, SiLU, down, weighted combine; optional shared expert with an
+// unmerged LoRA delta.
+//
+// Method (arXiv 2609.18063 as described on the pages):
+//  - the math contract every path shares: down(silu(gate(x)) * up(x))
+//    (jaehun.me review, report 3.1; koala.ai.kr execution paths);
+//  - "staged": fixed double-buffered slots, routing ids mapped through a slot
+//    table so indices never leave the GPU (koala.ai.kr paths table; jaehun.me
+//    report 3.1);
+//  - weighted combine over the top-K routed experts (jaehun.me report Appx. A
+//    routing weights);
+//  - shared expert with the recovery LoRA kept unmerged,
+//    y = W_int4 x + (alpha/r) B A x (xyznot.com adapter execution; jaehun.me
+//    report 3.3), LoRA on the shared-expert projections only (koala.ai.kr
+//    training phase 2).
+//
+// Kernels (one call = up to three launches on the caller's stream):
+//  1. prep   (grid L): per layer, a stable counting sort of the (token, k)
+//     pairs by expert (the deduplicated expert set and each expert's tokens),
+//     and the LoRA down-projections A x of the shared expert. Skipped when
+//     B == 1 and there is no LoRA.
+//  2. gateup (grid L x experts x row-chunks): each workgroup streams a block
+//     of gate and up rows of one expert once and applies them to all of its
+//     tokens: h = silu(gate x) * up x, written as fp32.
+//  3. down   (grid L x row-chunks): each workgroup owns a block of output
+//     rows of one layer and walks the layer's experts in a fixed order,
+//     accumulating w * (down h) per token; y is written once, no atomics.
+//
+// The int4 dot product: each lane holds 32 consecutive inputs of a row (one
+// 16-byte load of codes). Codes become fp16 16+q by bit placement
+// (exact), and v_dot2_f32_f16 accumulates (16+q) x in fp32; per lane and
+// group, s * acc + (b - 16 s) * sum(x) equals sum((s q + b) x). Row sums are
+// finished with a register reduce-scatter across the lanes of a row.
+#include "e0_internal.h"
+
+#include <math.h>
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kMaxB = 64;
+constexpr int kMaxK = 32;
+constexpr int kMaxE = 1024;
+constexpr int kMaxR = 32;
+constexpr int kDownRows = 64;  // output rows per down workgroup
+
+struct DecodeArgs {
+    int L, B, K, E, S, d, f;
+    const uint16_t *x;
+    const int32_t *idx;
+    const float *w;
+    const int32_t *slot_of;
+    Stack pool;
+    int has_shared;
+    Stack sh;
+    int r;
+    float lscale;
+    const uint16_t *la[3];
+    int64_t la_ls[3];
+    const uint16_t *lb[3];
+    int64_t lb_ls[3];
+    float *y;
+    int32_t *err;
+    int has_plan;
+    int umax;
+    int32_t *ucnt;   // [L]
+    int32_t *uexp;   // [L][umax]
+    int32_t *uslot;  // [L][umax]
+    int32_t *uoff;   // [L][umax + 1]
+    int32_t *pairs;  // [L][B*K]
+    float *hbuf;     // [L][B*K + B][f]
+    float *lora_a;   // [L][B][3][r]
+};
+
+E0_DEV int pairs_per_layer(const DecodeArgs &a) { return a.B * a.K + a.B; }
+
+E0_DEV float *hrow(const DecodeArgs &a, int l, int p) {
+    return a.hbuf + ((int64_t)l * pairs_per_layer(a) + p) * a.f;
+}
+
+E0_DEV float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------------------
+// Block-wide exclusive scan of one int per thread (256 threads).
+// ---------------------------------------------------------------------------
+E0_DEV int block_exclusive_scan(int v, int *lds4, int &total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+    }
+    if (lane == 63) lds4[wv] = inc;
+    __syncthreads();
+    int base = 0;
+    total = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        int t = lds4[i];
+        if (i < wv) base += t;
+        total += t;
+    }
+    __syncthreads();
+    return base + inc - v;
+}
+
+// ---------------------------------------------------------------------------
+// 1. prep: dedup plan + LoRA A x for the shared expert.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void decode_prep_kernel(DecodeArgs a) {
+    __shared__ int s_cnt[kMaxE];
+    __shared__ int s_base[kMaxE];
+    __shared__ int s_ids[kMaxB * kMaxK];
+    __shared__ int s_scan[kWaves];
+    const int l = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int n = a.B * a.K;
+
+    if (a.has_plan) {
+        for (int e = tid; e < a.E; e += kThreads) s_cnt[e] = 0;
+        __syncthreads();
+        for (int p = tid; p < n; p += kThreads) {
+            int e = a.idx[(int64_t)l * n + p];
+            if (e < 0 || e >= a.E) {
+                set_err(a.err, E0_DEV_BAD_ID);
+                e = -1;
+            } else {
+                atomicAdd(&s_cnt[e], 1);
+            }
+            s_ids[p] = e;
+        }
+        __syncthreads();
+        // Each thread owns E/256 consecutive experts (E <= 1024 -> up to 4).
+        const int per = (a.E + kThreads - 1) / kThreads;
+        const int e0 = tid * per;
+        int nu = 0, np = 0;
+        for (int e = e0; e < e0 + per && e < a.E; ++e) {
+            nu += s_cnt[e] > 0;
+            np += s_cnt[e];
+        }
+        int utot, ptot;
+        int ubase = block_exclusive_scan(nu, s_scan, utot);
+        int pbase = block_exclusive_scan(np, s_scan, ptot);
+        int32_t *uexp = a.uexp + (int64_t)l * a.umax;
+        int32_t *uslot = a.uslot + (int64_t)l * a.umax;
+        int32_t *uoff = a.uoff + (int64_t)l * (a.umax + 1);
+        for (int e = e0; e < e0 + per && e < a.E; ++e) {
+            s_base[e] = pbase;
+            if (s_cnt[e] > 0) {
+                uexp[ubase] = e;
+                uoff[ubase] = pbase;
+                int s = a.slot_of[(int64_t)l * a.E + e];
+                if (s < 0 || s >= a.S) {
+                    set_err(a.err, E0_DEV_NOT_RESIDENT);
+                    s = -1;
+                }
+                uslot[ubase] = s;
+                ++ubase;
+                pbase += s_cnt[e];
+            }
+        }
+        if (tid == 0) {
+            a.ucnt[l] = utot;
+            uoff[utot] = ptot;
+        }
+        __syncthreads();
+        // Stable placement: a pair's rank among earlier pairs of its expert.
+        int32_t *pairs = a.pairs + (int64_t)l * n;
+        for (int p = tid; p < n; p += kThreads) {
+            const int e = s_ids[p];
+            if (e < 0) continue;
+            int rank = 0;
+            for (int q = 0; q < p; ++q) rank += s_ids[q] == e;
+            pairs[s_base[e] + rank] = p;
+        }
+    }
+
+    if (a.has_shared && a.r > 0) {
+        // lora_a[l][t][p][i] = A_p[i] . x_t for gate and up (p = 0, 1).
+        const int lane = tid & 63, wv = tid >> 6;
+        const int jobs = a.B * 2 * a.r;
+        for (int job = wv; job < jobs; job += kWaves) {
+            const int t = job / (2 * a.r), rem = job % (2 * a.r), p = rem / a.r, i = rem % a.r;
+            const uint16_t *arow = a.la[p] + (int64_t)l * (a.la_ls[p] / 2) + (int64_t)i * a.d;
+            const uint16_t *xt = a.x + ((int64_t)l * a.B + t) * a.d;
+            float acc = 0.0f;
+            for (int c = lane * 8; c < a.d; c += 512) {
+                u32x4 av = *reinterpret_cast<const u32x4 *>(arow + c);
+                u32x4 xv = *reinterpret_cast<const u32x4 *>(xt + c);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc = __builtin_amdgcn_fdot2(as_h2(av[j]), as_h2(xv[j]),
+                                                 acc, false);
+            }
+            acc = wave_sum(acc);
+            if (lane == 0) a.lora_a[(((int64_t)l * a.B + t) * 3 + p) * a.r + i] = acc;
+        }
+    }
+}
+
+// Group reduce-scatter over aligned groups of G lanes (G a power of two).
+// N values per lane. After: if N >= G, lane holds N/G totals, index
+// (lane % G) * (N / G) + j, in v[0 .. N/G); else it holds one total in v[0],
+// index (lane % G) / (G / N). Stages are unrolled at compile time (M = the
+// lane distance, n = the live value count), so every register index is static.
+template <int N, int M, int n>
+struct ReduceStage {
+    static E0_DEV void run(float (&v)[N], int lane) {
+        if constexpr (n == 1) {
+            v[0] += __shfl_xor(v[0], M);
+        } else {
+            constexpr int h = n / 2;
+            const bool hi = (lane & M) != 0;
+#pragma unroll
+            for (int i = 0; i < h; ++i) {
+                const float keep = hi ? v[i + h] : v[i];
+                const float send = hi ? v[i] : v[i + h];
+                v[i] = keep + __shfl_xor(send, M);
+            }
+        }
+        if constexpr (M > 1) ReduceStage<N, M / 2, (n > 1 ? n / 2 : 1)>::run(v, lane);
+    }
+};
+
+template <int N, int G>
+E0_DEV void group_reduce_scatter(float (&v)[N]) {
+    if constexpr (G > 1) ReduceStage<N, G / 2, N>::run(v, threadIdx.x & 63);
+}
+
+// fp16 pairs (x_j, x_{j+4}) of 8 consecutive fp16 values held as 4 dwords.
+E0_DEV void x_pairs(const u32x4 v, uint32_t (&o)[4]) {
+    o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
+    o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
+    o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
+    o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
+}
+
+// sum over the 8 codes of `w` of (16 + q_c) * x_c, x given as pairs.
+E0_DEV float dot_word(uint32_t w, const uint32_t (&xp)[4], float acc) {
+    const uint32_t m = 0x03C003C0u, one6 = 0x4C004C00u;
+    const uint32_t t0 = ((w << 6) & m) | one6;
+    const uint32_t t1 = ((w << 2) & m) | one6;
+    const uint32_t t2 = ((w >> 2) & m) | one6;
+    const uint32_t t3 = ((w >> 6) & m) | one6;
+    acc = __builtin_amdgcn_fdot2(as_h2(t0), as_h2(xp[0]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(t1), as_h2(xp[1]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(t2), as_h2(xp[2]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(t3), as_h2(xp[3]), acc, false);
+    return acc;
+}
+
+// ---------------------------------------------------------------------------
+// 2. gateup. Template: LPR lanes per row pass (d = 32 * LPR * NP), TC tokens
+// per register chunk, RB rows per lane group per iteration.
+// ---------------------------------------------------------------------------
+template <int LPR, int NP, int TC, int RB>
+__global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
+    constexpr int RPI = kWave / LPR;          // rows per wave instruction
+    constexpr int ROWS_W = RPI * RB;          // rows per wave
+    constexpr int ROWS_B = ROWS_W * kWaves;   // rows per block
+    constexpr int NV = 2 * RB * TC;           // partial values per lane
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int gl = lane % LPR, grp = lane / LPR;
+    const int l = blockIdx.x, u = blockIdx.y;
+    const bool is_shared = a.has_shared && u == a.umax;
+
+    // Which expert, which slot, which pairs.
+    const Stack *st = is_shared ? &a.sh : &a.pool;
+    int slot = 0, p_begin = 0, p_count = 0;
+    const int32_t *plist = nullptr;
+    if (is_shared) {
+        p_begin = 0;
+        p_count = a.B;
+    } else if (a.has_plan) {
+        if (u >= a.ucnt[l]) return;
+        slot = a.uslot[(int64_t)l * a.umax + u];
+        if (slot < 0) return;
+        const int32_t *uoff = a.uoff + (int64_t)l * (a.umax + 1);
+        p_begin = uoff[u];
+        p_count = uoff[u + 1] - p_begin;
+        plist = a.pairs + (int64_t)l * a.B * a.K;
+    } else {
+        // B == 1: expert k of token 0.
+        const int e = a.idx[(int64_t)l * a.K + u];
+        if (e < 0 || e >= a.E) {
+            if (blockIdx.z == 0 && threadIdx.x == 0) set_err(a.err, E0_DEV_BAD_ID);
+            return;
+        }
+        slot = a.slot_of[(int64_t)l * a.E + e];
+        if (slot < 0 || slot >= a.S) {
+            if (blockIdx.z == 0 && threadIdx.x == 0) set_err(a.err, E0_DEV_NOT_RESIDENT);
+            return;
+        }
+        p_begin = u;
+        p_count = 1;
+    }
+    const int row_base = blockIdx.z * ROWS_B + wv * ROWS_W;
+    if (row_base >= a.f) return;
+
+    const int d = a.d;
+    const int ngrp = d / kGroup;
+    rsrc_t qr[2], sr[2], br[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        qr[m] = make_rsrc(part_at(st->p[3 * m + 0], l, slot), (uint32_t)a.f * d / 2);
+        sr[m] = make_rsrc(part_at(st->p[3 * m + 1], l, slot), (uint32_t)a.f * ngrp * 2);
+        br[m] = make_rsrc(part_at(st->p[3 * m + 2], l, slot), (uint32_t)a.f * ngrp * 2);
+    }
+
+    for (int c0 = 0; c0 < p_count; c0 += TC) {
+        // Token chunk: x slices as pairs, and their sums per pass.
+        int tok[TC];
+        int pid[TC];
+        uint32_t xp[TC][NP][4][4];
+        float xs[TC][NP];
+#pragma unroll
+        for (int t = 0; t < TC; ++t) {
+            const int ci = c0 + t;
+            int p = -1, tk = -1;
+            if (ci < p_count) {
+                if (is_shared) {
+                    tk = ci;
+                    p = a.B * a.K + ci;
+                } else if (plist) {
+                    p = plist[p_begin + ci];
+                    tk = p / a.K;
+                } else {
+                    p = p_begin;
+                    tk = 0;
+                }
+            }
+            tok[t] = tk;
+            pid[t] = p;
+            const int tl = tk >= 0 ? tk : 0;  // padding tokens read token 0; never written
+#pragma unroll
+            for (int np = 0; np < NP; ++np) {
+                float s = 0.0f;
+#pragma unroll
+                for (int wd = 0; wd < 4; ++wd) {
+                    const uint16_t *xr = a.x + ((int64_t)l * a.B + tl) * d + (np * LPR + gl) * 32 + wd * 8;
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(xr);
+                    x_pairs(v, xp[t][np][wd]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        f16x2 hv = as_h2(v[j]);
+                        s += (float)hv[0] + (float)hv[1];
+                    }
+                }
+                xs[t][np] = s;
+            }
+        }
+
+        float acc[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
+        // Rows in batches of RBB: the batch's code loads are issued together,
+        // then consumed; the scheduling fence keeps the compiler from hoisting
+        // every batch's loads at once (register pressure).
+        constexpr int RBB = RB < 4 ? RB : 4;
+#pragma unroll
+        for (int rb0 = 0; rb0 < RB; rb0 += RBB) {
+            u32x4 qv[RBB][2][NP];
+            float sv[RBB][2][NP], bv[RBB][2][NP];
+#pragma unroll
+            for (int rr = 0; rr < RBB; ++rr) {
+                // Rows past the end are clamped to the last row (in-bounds
+                // loads, results never written) so the loads stay unconditional.
+                const int row = min(row_base + (rb0 + rr) * RPI + grp, a.f - 1);
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                    for (int np = 0; np < NP; ++np) {
+                        const uint32_t col = (uint32_t)(np * LPR + gl);  // 32-element column block
+                        const uint32_t g = col / 2;                           // its group
+                        qv[rr][m][np] = ld128(qr[m], (uint32_t)row * (d / 2) + col * 16);
+                        sv[rr][m][np] = h2f(ld16(sr[m], ((uint32_t)row * ngrp + g) * 2));
+                        bv[rr][m][np] = h2f(ld16(br[m], ((uint32_t)row * ngrp + g) * 2));
+                    }
+                }
+            }
+#pragma unroll
+            for (int rr = 0; rr < RBB; ++rr) {
+                const int rb = rb0 + rr;
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                    for (int np = 0; np < NP; ++np) {
+                        const float s = sv[rr][m][np];
+                        const float b16 = bv[rr][m][np] - 16.0f * s;
+#pragma unroll
+                        for (int t = 0; t < TC; ++t) {
+                            float dacc = 0.0f;
+#pragma unroll
+                            for (int wd = 0; wd < 4; ++wd) dacc = dot_word(qv[rr][m][np][wd], xp[t][np][wd], dacc);
+                            acc[(m * RB + rb) * TC + t] += s * dacc + b16 * xs[t][np];
+                        }
+                    }
+                }
+            }
+            __asm__ __volatile__("" ::: "memory");  // keep batches apart (register pressure)
+        }
+
+        group_reduce_scatter<NV, LPR>(acc);
+
+        // Each lane now holds totals; gate values in the lower half of a row
+        // group, up values in the upper half (partner lane ^ LPR/2).
+        constexpr int PER = NV >= LPR ? NV / LPR : 1;
+        constexpr int DUP = NV >= LPR ? 1 : LPR / NV;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int vi = NV >= LPR ? gl * PER + j : gl / DUP;  // value index
+            const int m = vi / (RB * TC);
+            const int rb = (vi / TC) % RB;
+            const int t = vi % TC;
+            float val = acc[j];
+            const int row = row_base + rb * RPI + grp;
+            if (is_shared && a.r > 0 && row < a.f && tok[t] >= 0) {
+                const uint16_t *brow = a.lb[m] + (int64_t)l * (a.lb_ls[m] / 2) + (int64_t)row * a.r;
+                const float *av = a.lora_a + (((int64_t)l * a.B + tok[t]) * 3 + m) * a.r;
+                float dl = 0.0f;
+                for (int i = 0; i < a.r; ++i) dl += h2f(brow[i]) * av[i];
+                val += a.lscale * dl;
+            }
+            const float other = __shfl_xor(val, LPR / 2);
+            if (m == 0 && (NV >= LPR || gl % DUP == 0) && row < a.f && tok[t] >= 0)
+                hrow(a, l, pid[t])[row] = silu(val) * other;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. down + weighted combine. LPR lanes per row (f = 32 * LPR), RPI rows per
+// wave instruction, IT instructions per wave (kDownRows rows per block).
+// ---------------------------------------------------------------------------
+template <int LPR>
+struct DownCfg {
+    static constexpr int RPI = kWave / LPR;
+    static constexpr int IT = kDownRows / (kWaves * RPI) > 0 ? kDownRows / (kWaves * RPI) : 1;
+};
+
+// Partial dot of one row pass: sum over the lane's 32 columns of (s q + b) h.
+E0_DEV float down_dot(const u32x4 qv, float s, float b, const float (&h)[32], float hsum) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+        const uint32_t w = qv[wd];
+        const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            acc += (float)((lo >> (8 * k)) & 0xFFu) * h[wd * 8 + 2 * k];
+            acc += (float)((hi >> (8 * k)) & 0xFFu) * h[wd * 8 + 2 * k + 1];
+        }
+    }
+    return s * acc + b * hsum;
+}
+
+template <int LPR>
+__global__ __launch_bounds__(kThreads) void decode_down_kernel(DecodeArgs a) {
+    constexpr int RPI = DownCfg<LPR>::RPI;
+    constexpr int IT = DownCfg<LPR>::IT;
+    __shared__ float s_acc[kMaxB][kDownRows];
+    __shared__ float s_lora[kMaxB][kMaxR];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int gl = lane % LPR, grp = lane / LPR;
+    const int l = blockIdx.x;
+    const int row0 = blockIdx.y * kDownRows;
+    const int f = a.f, d = a.d;
+    const int fgrp = f / kGroup;
+    const int col0 = gl * 32;
+    const int g = col0 / kGroup;
+    int rows[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) rows[it] = row0 + (wv * IT + it) * RPI + grp;
+
+    // Shared-expert LoRA: a_d[t] = A_down h_shared[t] (r values per token).
+    const bool lora = a.has_shared && a.r > 0;
+    if (lora) {
+        const int jobs = a.B * a.r;
+        for (int job = wv; job < jobs; job += kWaves) {
+            const int t = job / a.r, i = job % a.r;
+            const uint16_t *arow = a.la[2] + (int64_t)l * (a.la_ls[2] / 2) + (int64_t)i * f;
+            const float *hs = hrow(a, l, a.B * a.K + t);
+            float acc = 0.0f;
+            for (int c = lane; c < f; c += kWave) acc += h2f(arow[c]) * hs[c];
+            acc = wave_sum(acc);
+            if (lane == 0) s_lora[t][i] = acc;
+        }
+        __syncthreads();
+    }
+
+    // One expert's contribution to this lane's rows for pair p, weight wk.
+    auto expert_rows = [&](const Stack &st, int slot, int p, float wk, float (&out)[IT]) {
+        const rsrc_t qb = make_rsrc(part_at(st.p[6], l, slot), (uint32_t)d * f / 2);
+        const rsrc_t sb = make_rsrc(part_at(st.p[7], l, slot), (uint32_t)d * fgrp * 2);
+        const rsrc_t bb = make_rsrc(part_at(st.p[8], l, slot), (uint32_t)d * fgrp * 2);
+        const float *hp = hrow(a, l, p) + col0;
+        float h[32];
+        float hsum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            f32x4 v = *reinterpret_cast<const f32x4 *>(hp + 4 * i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                h[4 * i + j] = v[j];
+                hsum += v[j];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const uint32_t row = (uint32_t)min(rows[it], d - 1);  // clamped: in-bounds, never written
+            const u32x4 qv = ld128(qb, row * (f / 2) + gl * 16);
+            const float s = h2f(ld16(sb, (row * fgrp + g) * 2));
+            const float b = h2f(ld16(bb, (row * fgrp + g) * 2));
+            out[it] += wk * down_dot(qv, s, b, h, hsum);
+        }
+    };
+
+    if (!a.has_plan) {
+        // B == 1: experts in k order, then the shared expert.
+        float acc[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) acc[it] = 0.0f;
+        for (int k = 0; k < a.K; ++k) {
+            const int e = a.idx[(int64_t)l * a.K + k];
+            if (e < 0 || e >= a.E) continue;
+            const int slot = a.slot_of[(int64_t)l * a.E + e];
+            if (slot < 0 || slot >= a.S) continue;
+            expert_rows(a.pool, slot, k, a.w[(int64_t)l * a.K + k], acc);
+        }
+        if (a.has_shared) expert_rows(a.sh, 0, a.K, 1.0f, acc);
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            float v = group_sum(acc[it], LPR);
+            const int row = rows[it];
+            if (lora && row < d) {
+                const uint16_t *brow = a.lb[2] + (int64_t)l * (a.lb_ls[2] / 2) + (int64_t)row * a.r;
+                float dl = 0.0f;
+                for (int i = 0; i < a.r; ++i) dl += h2f(brow[i]) * s_lora[0][i];
+                v += a.lscale * dl;
+            }
+            if (gl == 0 && row < d) a.y[(int64_t)l * d + row] = v;
+        }
+        return;
+    }
+
+    // B > 1: unique experts in ascending id, each pair's contribution folded
+    // into the block's per-token accumulators in that order.
+    for (int i = threadIdx.x; i < a.B * kDownRows; i += kThreads) s_acc[i / kDownRows][i % kDownRows] = 0.0f;
+    __syncthreads();
+    const int nu = a.ucnt[l];
+    const int32_t *uoff = a.uoff + (int64_t)l * (a.umax + 1);
+    const int32_t *plist = a.pairs + (int64_t)l * a.B * a.K;
+    auto fold = [&](float (&part)[IT], int t) {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const float v = group_sum(part[it], LPR);
+            const int row = rows[it];
+            if (gl == 0 && row < d) s_acc[t][row - row0] += v;
+        }
+    };
+    for (int u = 0; u < nu; ++u) {
+        const int slot = a.uslot[(int64_t)l * a.umax + u];
+        if (slot < 0) continue;
+        for (int pi = uoff[u]; pi < uoff[u + 1]; ++pi) {
+            const int p = plist[pi];
+            float part[IT];
+#pragma unroll
+            for (int it = 0; it < IT; ++it) part[it] = 0.0f;
+            expert_rows(a.pool, slot, p, a.w[(int64_t)l * a.B * a.K + p], part);
+            fold(part, p / a.K);
+        }
+    }
+    if (a.has_shared) {
+        for (int t = 0; t < a.B; ++t) {
+            float part[IT];
+#pragma unroll
+            for (int it = 0; it < IT; ++it) part[it] = 0.0f;
+            expert_rows(a.sh, 0, a.B * a.K + t, 1.0f, part);
+            fold(part, t);
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.B * kDownRows; i += kThreads) {
+        const int t = i / kDownRows, rr = i % kDownRows, row = row0 + rr;
+        if (row >= d) continue;
+        float v = s_acc[t][rr];
+        if (lora) {
+            const uint16_t *brow = a.lb[2] + (int64_t)l * (a.lb_ls[2] / 2) + (int64_t)row * a.r;
+            float dl = 0.0f;
+            for (int j = 0; j < a.r; ++j) dl += h2f(brow[j]) * s_lora[t][j];
+            v += a.lscale * dl;
+        }
+        a.y[((int64_t)l * a.B + t) * d + row] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Supported d_model: 256 .. 2048 powers of two, or multiples of 2048 up to 8192.
+int d_lpr(int d, int &np) {
+    if (d >= 256 && d <= 2048 && pow2(d)) {
+        np = 1;
+        return d / 32;
+    }
+    if (d > 2048 && d % 2048 == 0 && d <= 8192) {
+        np = d / 2048;
+        return 64;
+    }
+    return 0;
+}
+
+// Supported d_ff: 128 .. 2048 powers of two.
+int f_lpr(int f) { return (f >= 128 && f <= 2048 && pow2(f)) ? f / 32 : 0; }
+
+struct Layout {
+    size_t ucnt, uexp, uslot, uoff, pairs, hbuf, lora, total;
+};
+
+Layout decode_layout(int L, int B, int K, int E, int f, int r) {
+    Layout o;
+    const int umax = B == 1 ? K : (E < B * K ? E : B * K);
+    size_t off = 0;
+    o.ucnt = off;
+    off = e0_align(off + sizeof(int32_t) * L);
+    o.uexp = off;
+    off = e0_align(off + sizeof(int32_t) * (size_t)L * umax);
+    o.uslot = off;
+    off = e0_align(off + sizeof(int32_t) * (size_t)L * umax);
+    o.uoff = off;
+    off = e0_align(off + sizeof(int32_t) * (size_t)L * (umax + 1));
+    o.pairs = off;
+    off = e0_align(off + sizeof(int32_t) * (size_t)L * B * K);
+    o.hbuf = off;
+    off = e0_align(off + sizeof(float) * (size_t)L * (B * K + B) * f);
+    o.lora = off;
+    off = e0_align(off + sizeof(float) * (size_t)L * B * 3 * (r > 0 ? r : 1));
+    o.total = off;
+    return o;
+}
+
+template <int LPR, int NP, int TC, int RB>
+void launch_gateup(const DecodeArgs &a, dim3 grid, hipStream_t st) {
+    hipLaunchKernelGGL((decode_gateup_kernel<LPR, NP, TC, RB>), grid, dim3(kThreads), 0, st, a);
+}
+
+template <int TC, int RB>
+bool dispatch_gateup(int lpr, int np, const DecodeArgs &a, dim3 grid, hipStream_t st) {
+    switch (lpr * 8 + np) {
+        case 8 * 8 + 1: launch_gateup<8, 1, TC, RB>(a, grid, st); return true;
+        case 16 * 8 + 1: launch_gateup<16, 1, TC, RB>(a, grid, st); return true;
+        case 32 * 8 + 1: launch_gateup<32, 1, TC, RB>(a, grid, st); return true;
+        case 64 * 8 + 1: launch_gateup<64, 1, TC, RB>(a, grid, st); return true;
+        case 64 * 8 + 2: launch_gateup<64, 2, TC, RB>(a, grid, st); return true;
+        case 64 * 8 + 3: launch_gateup<64, 3, TC, RB>(a, grid, st); return true;
+        case 64 * 8 + 4: launch_gateup<64, 4, TC, RB>(a, grid, st); return true;
+        default: return false;
+    }
+}
+
+template <int TC, int RB>
+int gateup_rows_per_block(int lpr) {
+    return (kWave / lpr) * RB * kWaves;
+}
+
+bool dispatch_down(int lpr, const DecodeArgs &a, dim3 grid, hipStream_t st) {
+    switch (lpr) {
+        case 4: hipLaunchKernelGGL(decode_down_kernel<4>, grid, dim3(kThreads), 0, st, a); return true;
+        case 8: hipLaunchKernelGGL(decode_down_kernel<8>, grid, dim3(kThreads), 0, st, a); return true;
+        case 16: hipLaunchKernelGGL(decode_down_kernel<16>, grid, dim3(kThreads), 0, st, a); return true;
+        case 32: hipLaunchKernelGGL(decode_down_kernel<32>, grid, dim3(kThreads), 0, st, a); return true;
+        case 64: hipLaunchKernelGGL(decode_down_kernel<64>, grid, dim3(kThreads), 0, st, a); return true;
+        default: return false;
+    }
+}
+
+bool stack_ok(const e0_stack *s, int first, int last) {
+    for (int i = first; i <= last; ++i) {
+        const e0_part &p = s->part[i];
+        if (!p.ptr) return false;
+        if ((reinterpret_cast<uintptr_t>(p.ptr) | (uintptr_t)p.slot_stride | (uintptr_t)p.layer_stride) & 15)
+            return false;
+    }
+    return true;
+}
+
+}  // namespace
+
+size_t e0_decode_workspace_bytes(const e0_moe_dims *dims, int32_t L, int32_t B, int32_t r) {
+    if (!dims || L < 0 || B < 1) return 0;
+    return decode_layout(L, B, dims->top_k, dims->n_experts, dims->d_ff, r).total;
+}
+
+extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, int32_t B, const uint16_t *x,
+                                          const int32_t *idx, const float *w, const int32_t *slot_of, int32_t S,
+                                          const e0_stack *pool, const e0_shared *shared, float *y, void *ws,
+                                          size_t ws_bytes, int32_t *dev_err, void *stream) {
+    E0_REQUIRE(dims && pool, E0_ERR_INVALID_ARG);
+    const int d = dims->d_model, f = dims->d_ff, E = dims->n_experts, K = dims->top_k;
+    E0_REQUIRE(L >= 0 && B >= 1 && S >= 1 && E >= 1 && K >= 1, E0_ERR_INVALID_ARG);
+    E0_REQUIRE(d % 64 == 0 && f % 64 == 0, E0_ERR_UNSUPPORTED_SHAPE);
+    int np = 0;
+    const int lpr_d = d_lpr(d, np), lpr_f = f_lpr(f);
+    E0_REQUIRE(lpr_d && lpr_f, E0_ERR_UNSUPPORTED_SHAPE);
+    E0_REQUIRE(K <= kMaxK && K <= E && E <= kMaxE, E0_ERR_UNSUPPORTED_SHAPE);
+    E0_REQUIRE(B <= kMaxB, E0_ERR_CAPACITY);
+    E0_REQUIRE(x && idx && w && slot_of && y && dev_err, E0_ERR_INVALID_ARG);
+    E0_REQUIRE(stack_ok(pool, 0, 8), E0_ERR_INVALID_ARG);
+    E0_REQUIRE((reinterpret_cast<uintptr_t>(x) & 15) == 0, E0_ERR_INVALID_ARG);
+    int r = 0;
+    if (shared) {
+        E0_REQUIRE(stack_ok(&shared->w, 0, 8), E0_ERR_INVALID_ARG);
+        E0_REQUIRE(shared->d_ff == f, E0_ERR_UNSUPPORTED_SHAPE);
+        r = shared->lora_rank;
+        E0_REQUIRE(r >= 0 && r <= kMaxR, E0_ERR_UNSUPPORTED_SHAPE);
+        if (r > 0) {
+            for (int p = 0; p < 3; ++p) {
+                E0_REQUIRE(shared->lora_a[p] && shared->lora_b[p], E0_ERR_INVALID_ARG);
+                E0_REQUIRE(((reinterpret_cast<uintptr_t>(shared->lora_a[p]) | (uintptr_t)shared->lora_a_layer_stride[p]) & 15) == 0,
+                           E0_ERR_INVALID_ARG);
+                E0_REQUIRE((shared->lora_b_layer_stride[p] & 1) == 0, E0_ERR_INVALID_ARG);
+            }
+        }
+    }
+    const Layout lay = decode_layout(L, B, K, E, f, r);
+    E0_REQUIRE(ws && ws_bytes >= lay.total && (reinterpret_cast<uintptr_t>(ws) & 255) == 0, E0_ERR_CAPACITY);
+    if (L == 0) return E0_OK;
+
+    DecodeArgs a{};
+    a.L = L;
+    a.B = B;
+    a.K = K;
+    a.E = E;
+    a.S = S;
+    a.d = d;
+    a.f = f;
+    a.x = x;
+    a.idx = idx;
+    a.w = w;
+    a.slot_of = slot_of;
+    a.pool = to_stack(*pool);
+    a.has_shared = shared != nullptr;
+    if (shared) {
+        a.sh = to_stack(shared->w);
+        a.r = r;
+        a.lscale = shared->lora_scale;
+        for (int p = 0; p < 3; ++p) {
+            a.la[p] = shared->lora_a[p];
+            a.la_ls[p] = shared->lora_a_layer_stride[p];
+            a.lb[p] = shared->lora_b[p];
+            a.lb_ls[p] = shared->lora_b_layer_stride[p];
+        }
+    }
+    a.y = y;
+    a.err = dev_err;
+    a.has_plan = B > 1;
+    a.umax = B == 1 ? K : (E < B * K ? E : B * K);
+    char *wsb = static_cast<char *>(ws);
+    a.ucnt = reinterpret_cast<int32_t *>(wsb + lay.ucnt);
+    a.uexp = reinterpret_cast<int32_t *>(wsb + lay.uexp);
+    a.uslot = reinterpret_cast<int32_t *>(wsb + lay.uslot);
+    a.uoff = reinterpret_cast<int32_t *>(wsb + lay.uoff);
+    a.pairs = reinterpret_cast<int32_t *>(wsb + lay.pairs);
+    a.hbuf = reinterpret_cast<float *>(wsb + lay.hbuf);
+    a.lora_a = reinterpret_cast<float *>(wsb + lay.lora);
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    e0_status s;
+    if (a.has_plan || (a.has_shared && r > 0)) {
+        hipLaunchKernelGGL(decode_prep_kernel, dim3(L), dim3(kThreads), 0, st, a);
+        if ((s = e0_launch_status())) return s;
+    }
+    const int ublocks = a.umax + (a.has_shared ? 1 : 0);
+    if (B == 1) {
+        constexpr int TC = 1, RB = 16;
+        const int rpb = gateup_rows_per_block<TC, RB>(lpr_d);
+        dim3 grid(L, ublocks, (f + rpb - 1) / rpb);
+        const bool ok = dispatch_gateup<TC, RB>(lpr_d, np, a, grid, st);
+        E0_REQUIRE(ok, E0_ERR_UNSUPPORTED_SHAPE);
+    } else {
+        constexpr int TC = 4, RB = 4;
+        const int rpb = gateup_rows_per_block<TC, RB>(lpr_d);
+        dim3 grid(L, ublocks, (f + rpb - 1) / rpb);
+        const bool ok = dispatch_gateup<TC, RB>(lpr_d, np, a, grid, st);
+        E0_REQUIRE(ok, E0_ERR_UNSUPPORTED_SHAPE);
+    }
+    if ((s = e0_launch_status())) return s;
+    E0_REQUIRE(dispatch_down(lpr_f, a, dim3(L, (d + kDownRows - 1) / kDownRows), st), E0_ERR_UNSUPPORTED_SHAPE);
+    return e0_launch_status();
+}

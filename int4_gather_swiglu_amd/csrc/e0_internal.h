@@ -1,0 +1,123 @@
+// Internal helpers shared by the gfx950 kernels of libe0 (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/e0.h"
+
+#define E0_DEV __device__ __forceinline__
+
+typedef _Float16 f16;
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kGroup = 64;  // quantisation group along the input dimension
+
+// A part of a stacked tensor, as kernels see it.
+struct Part {
+    const char *ptr;
+    int64_t slot_stride;
+    int64_t layer_stride;
+};
+
+struct Stack {
+    Part p[9];  // [3 * matrix + kind]; matrix 0 gate, 1 up, 2 down; kind 0 q, 1 s, 2 b
+};
+
+inline Stack to_stack(const e0_stack &s) {
+    Stack o;
+    for (int i = 0; i < 9; ++i) {
+        o.p[i].ptr = static_cast<const char *>(s.part[i].ptr);
+        o.p[i].slot_stride = s.part[i].slot_stride;
+        o.p[i].layer_stride = s.part[i].layer_stride;
+    }
+    return o;
+}
+
+E0_DEV const char *part_at(const Part &p, int layer, int slot) {
+    return p.ptr + (int64_t)layer * p.layer_stride + (int64_t)slot * p.slot_stride;
+}
+
+E0_DEV float h2f(uint16_t b) { return (float)__builtin_bit_cast(f16, b); }
+
+// Reinterpret a dword as two fp16. Takes the dword by value: applying
+// __builtin_bit_cast directly to an element of an ext_vector (v[j]) reads the
+// vector's first element whatever j is, so every such cast goes through here.
+E0_DEV f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+
+// Raw buffer resources: an SGPR descriptor over `bytes` bytes at `p`, loaded
+// with 32-bit per-lane byte offsets (no 64-bit address registers per load).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;
+E0_DEV rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcFlags);
+}
+E0_DEV u32x4 ld128(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0); }
+E0_DEV uint16_t ld16(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0); }
+
+E0_DEV float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+E0_DEV float group_sum(float v, int width) {
+    for (int m = width >> 1; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+// Reduce-scatter of N values held by each of 64 lanes (N a power of two,
+// 32 <= N). After the call, lane l holds in v[0 .. N/64) the totals of value
+// indices l*(N/64) + j for N >= 64; for N == 32 lane l holds in v[0] the total
+// of index l >> 1.
+template <int N>
+E0_DEV void wave_reduce_scatter(float (&v)[N]) {
+    const int lane = threadIdx.x & 63;
+    int n = N;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        if (n == 1) {
+            v[0] += __shfl_xor(v[0], m);
+            continue;
+        }
+        const bool hi = (lane & m) != 0;
+        const int h = n >> 1;
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            if (i < h) {
+                float keep = hi ? v[i + h] : v[i];
+                float send = hi ? v[i] : v[i + h];
+                v[i] = keep + __shfl_xor(send, m);
+            }
+        }
+        n = h;
+    }
+}
+
+// Orders LDS accesses of one wavefront (lanes exchange values through LDS).
+E0_DEV void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+E0_DEV void set_err(int32_t *err, int bits) {
+    if (err) atomicOr(err, bits);
+}
+
+// Status plumbing for host entry points.
+#define E0_REQUIRE(cond, code) \
+    do {                       \
+        if (!(cond)) return (code); \
+    } while (0)
+
+inline e0_status e0_launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? E0_OK : E0_ERR_HIP;
+}
+
+inline size_t e0_align(size_t x) { return (x + 255) & ~(size_t)255; }

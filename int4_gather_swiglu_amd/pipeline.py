@@ -1,0 +1,73 @@
+"""Staged decode pipeline: the C-ABI calls of one decode step, sequenced on
+HIP streams. Holds device buffers; computes nothing itself.
+
+Per step t (fixed double-buffered slots, routing ids kept on the GPU; the
+update for step t+1 overlaps step t: koala.ai.kr paths table and Fig. 1
+timeline; jaehun.me review, report 3.1):
+
+  main : routing of step t+1          -> idx[(t+1) % 2]   (e0_route or e0_prerouter)
+  side : (waits for it) slot update   next = idx[(t+1) % 2], in use = idx[t % 2]
+  main : staged decode of step t      reads idx[t % 2] through the slot table
+  main : (before step t+1) waits for the side stream
+
+The update only writes slots whose experts are in neither set, and leaves the
+slot-table entries of step t's experts untouched, so it can run while step t
+reads the pool.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as E
+
+
+class StagedPipeline:
+    def __init__(self, dims: E.MoeDims, L: int, B: int, S: int, store: E.Stack, pool: E.Stack,
+                 shared: E.Shared | None = None, device="cuda", side_stream: bool = True):
+        self.dims, self.L, self.B, self.S = dims, L, B, S
+        self.store, self.pool, self.shared = store, pool, shared
+        K, Ex = dims.top_k, dims.n_experts
+        dev = torch.device(device)
+        self.dev = dev
+        self.slot_of = torch.full((L, Ex), -1, dtype=torch.int32, device=dev)
+        self.expert_of = torch.full((L, S), -1, dtype=torch.int32, device=dev)
+        self.idx = torch.zeros((2, L, B, K), dtype=torch.int32, device=dev)
+        self.w = torch.zeros((2, L, B, K), dtype=torch.float32, device=dev)
+        self.n_copied = torch.zeros((L,), dtype=torch.int32, device=dev)
+        self.err = torch.zeros((1,), dtype=torch.int32, device=dev)
+        r = shared.lora_rank if shared is not None else 0
+        self.ws_dec = torch.empty(E.workspace_bytes(E.E0_OP_STAGED_DECODE, dims, L, B, r), dtype=torch.uint8,
+                                  device=dev)
+        self.ws_slot = torch.empty(E.workspace_bytes(E.E0_OP_SLOT_UPDATE, dims, L, B, S), dtype=torch.uint8,
+                                   device=dev)
+        self.main = torch.cuda.current_stream(dev)
+        self.side = torch.cuda.Stream(dev) if side_stream else self.main
+        self.ev_routed = torch.cuda.Event()
+        self.ev_updated = torch.cuda.Event()
+
+    # -- pieces -------------------------------------------------------------
+    def route_given(self, buf: int, params: E.RouteParams, logits, fp16: bool = True):
+        """Route step logits [L][B][E] (fp16 bits or fp32) into idx/w[buf]."""
+        E.e0_route(params, self.L, self.B, self.dims.n_experts, logits, fp16, None, None, 0, self.idx[buf],
+                   self.w[buf], None, stream=self.main)
+
+    def route_router(self, buf: int, params: E.RouteParams, x, w_router, logits_out):
+        """Route with each layer's own router over x [L][B][d]."""
+        E.e0_route(params, self.L, self.B, self.dims.n_experts, None, False, x, w_router, self.dims.d_model,
+                   self.idx[buf], self.w[buf], logits_out, stream=self.main)
+
+    def update(self, nxt: int, cur: int | None):
+        """Slot update for idx[nxt], protecting idx[cur], on the side stream."""
+        self.ev_routed.record(self.main)
+        self.side.wait_event(self.ev_routed)
+        E.e0_slot_update(self.dims, self.L, self.B, self.S, self.idx[nxt], None if cur is None else self.idx[cur],
+                         self.slot_of, self.expert_of, self.store, self.pool, self.n_copied, self.ws_slot, self.err,
+                         stream=self.side)
+        self.ev_updated.record(self.side)
+
+    def join(self):
+        self.main.wait_event(self.ev_updated)
+
+    def decode(self, buf: int, x, y):
+        E.e0_moe_staged_decode(self.dims, self.L, self.B, x, self.idx[buf], self.w[buf], self.slot_of, self.S,
+                               self.pool, self.shared, y, self.ws_dec, self.err, stream=self.main)

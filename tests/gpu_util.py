@@ -1,0 +1,63 @@
+"""Helpers for the GPU parity tests: device buffers from generated inputs."""
+from __future__ import annotations
+
+import numpy as np
+
+from e0inputs import gen
+
+
+def torch():
+    import torch as T
+    return T
+
+
+def dev():
+    return torch().device("cuda:0")
+
+
+def f16(a: np.ndarray):
+    """fp16 numpy array -> int16 device tensor with the same bits."""
+    return torch().from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev())
+
+
+def i32(a):
+    return torch().from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.int32))).to(dev())
+
+
+def f32(a):
+    return torch().from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.float32))).to(dev())
+
+
+def empty(shape, dtype="float32"):
+    T = torch()
+    return T.empty(shape, dtype=getattr(T, dtype), device=dev())
+
+
+def zeros(shape, dtype="float32"):
+    T = torch()
+    return T.zeros(shape, dtype=getattr(T, dtype), device=dev())
+
+
+def full(shape, v, dtype="int32"):
+    T = torch()
+    return T.full(shape, v, dtype=getattr(T, dtype), device=dev())
+
+
+def gpu_store(cfg, layers, tag=gen.TAG_EXPERT):
+    """uint8 [len(layers)][E][bundle] device tensor filled on the GPU."""
+    from e0inputs import gpu as G
+    bb = gen.bundle_bytes(cfg.d, cfg.f)
+    st = zeros((len(layers), cfg.E, bb), "uint8")
+    for i, l in enumerate(layers):
+        G.fill_experts(st[i].data_ptr(), bb, cfg.seed, l, range(cfg.E), cfg.d, cfg.f, tag)
+    return st
+
+
+def rel_l2(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def bytes_of(t):
+    return t.numel() * t.element_size()

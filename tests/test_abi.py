@@ -1,0 +1,143 @@
+"""C ABI: the library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching the GPU (no kernel is launched by any
+case here: each one fails validation)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from int4_gather_swiglu_amd import _lib as E
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "e0.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:e0_status|int32_t|const char \*|size_t)\s*\n?\s*(e0_\w+)\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    L = E.lib()
+    names = _declared()
+    assert set(names) == set(E.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_version_and_strings():
+    assert E.abi_version() == 1
+    assert E.status_string(0) == "ok"
+    assert "workspace" in E.status_string(E.E0_ERR_CAPACITY)
+    assert E.status_string(99) == "unknown status"
+
+
+def test_workspace_sizes():
+    dims = E.moe_dims(2048, 512, 256, 4)
+    assert E.workspace_bytes(E.E0_OP_ROUTE, dims, 10) == 0
+    assert E.workspace_bytes(E.E0_OP_STAGED_DECODE, dims, 40, 1, 0) >= 40 * 5 * 512 * 4
+    assert E.workspace_bytes(E.E0_OP_SLOT_UPDATE, dims, 40, 1, 8) > 0
+    assert E.workspace_bytes(E.E0_OP_STAGED_DECODE, dims, 40, 0, 0) == 0
+    assert E.workspace_bytes(99, dims, 1) == 0
+
+
+def _route(params, L=1, T=1, Ex=16, logits=FAKE, fp16=0, x=None, wr=None, d=0, idx=FAKE, w=FAKE, lo=None):
+    return E.lib().e0_route(C.byref(params), L, T, Ex, C.c_void_p(logits) if logits else None, fp16,
+                            C.c_void_p(x) if x else None, C.c_void_p(wr) if wr else None, d,
+                            C.c_void_p(idx) if idx else None, C.c_void_p(w) if w else None,
+                            C.c_void_p(lo) if lo else None, None)
+
+
+def test_route_validation():
+    assert E.lib().e0_route(None, 1, 1, 16, None, 0, None, None, 0, None, None, None, None) == E.E0_ERR_INVALID_ARG
+    assert _route(E.route_params(2, 4)) == E.E0_ERR_INVALID_ARG              # bad mode
+    assert _route(E.route_params(0, 17), Ex=16) == E.E0_ERR_UNSUPPORTED_SHAPE  # K > E
+    assert _route(E.route_params(0, 4), Ex=2048) == E.E0_ERR_UNSUPPORTED_SHAPE
+    assert _route(E.route_params(1, 4, 3, 2, 2.5), Ex=16) == E.E0_ERR_UNSUPPORTED_SHAPE  # groups do not divide E
+    assert _route(E.route_params(1, 9, 8, 4, 2.5), Ex=16) == E.E0_ERR_UNSUPPORTED_SHAPE  # K > kept experts
+    assert _route(E.route_params(0, 4), idx=None) == E.E0_ERR_INVALID_ARG
+    # router path: logits_out required, d a multiple of 64
+    assert _route(E.route_params(0, 4), logits=None, x=FAKE, wr=FAKE, d=256) == E.E0_ERR_INVALID_ARG
+    assert _route(E.route_params(0, 4), logits=None, x=FAKE, wr=FAKE, d=100, lo=FAKE) == E.E0_ERR_UNSUPPORTED_SHAPE
+
+
+def _stack(addr=FAKE, stride=1 << 20):
+    st = E.Stack()
+    for i in range(9):
+        st.part[i] = E.Part(addr + 4096 * i, stride, 0)
+    return st
+
+
+def _decode(dims, L=1, B=1, S=8, ws_bytes=1 << 30, pool=None, shared=None, x=FAKE, err=FAKE):
+    pool = pool or _stack()
+    return E.lib().e0_moe_staged_decode(C.byref(dims), L, B, C.c_void_p(x) if x else None, C.c_void_p(FAKE),
+                                        C.c_void_p(FAKE), C.c_void_p(FAKE), S, C.byref(pool),
+                                        C.byref(shared) if shared else None, C.c_void_p(FAKE),
+                                        C.c_void_p(FAKE), ws_bytes, C.c_void_p(err) if err else None, None)
+
+
+def test_decode_validation():
+    assert _decode(E.moe_dims(100, 512, 256, 4)) == E.E0_ERR_UNSUPPORTED_SHAPE      # d % 64
+    assert _decode(E.moe_dims(2048, 96, 256, 4)) == E.E0_ERR_UNSUPPORTED_SHAPE      # f % 64 ok, not supported width
+    assert _decode(E.moe_dims(2048, 512, 4, 8)) == E.E0_ERR_UNSUPPORTED_SHAPE       # K > E
+    assert _decode(E.moe_dims(2048, 512, 256, 4), B=65) == E.E0_ERR_CAPACITY         # B limit
+    assert _decode(E.moe_dims(2048, 512, 256, 4), ws_bytes=16) == E.E0_ERR_CAPACITY  # workspace
+    assert _decode(E.moe_dims(2048, 512, 256, 4), x=None) == E.E0_ERR_INVALID_ARG
+    assert _decode(E.moe_dims(2048, 512, 256, 4), err=None) == E.E0_ERR_INVALID_ARG
+    assert _decode(E.moe_dims(2048, 512, 256, 4), pool=_stack(FAKE + 4)) == E.E0_ERR_INVALID_ARG  # misaligned
+    sh = E.Shared()
+    sh.w = _stack()
+    sh.d_ff = 256
+    assert _decode(E.moe_dims(2048, 512, 256, 4), shared=sh) == E.E0_ERR_UNSUPPORTED_SHAPE  # shared width differs
+    sh.d_ff = 512
+    sh.lora_rank = 64
+    assert _decode(E.moe_dims(2048, 512, 256, 4), shared=sh) == E.E0_ERR_UNSUPPORTED_SHAPE
+
+
+def test_slot_update_validation():
+    dims = E.moe_dims(2048, 512, 256, 4)
+    L = E.lib()
+    ok_stack = _stack()
+
+    def call(dims=dims, S=8, ws_bytes=1 << 20, nxt=FAKE, store=ok_stack):
+        return L.e0_slot_update(C.byref(dims), 1, 1, S, C.c_void_p(nxt) if nxt else None, None, C.c_void_p(FAKE),
+                                C.c_void_p(FAKE), C.byref(store), C.byref(ok_stack), None, C.c_void_p(FAKE),
+                                ws_bytes, C.c_void_p(FAKE), None)
+    assert call(S=0) == E.E0_ERR_INVALID_ARG
+    assert call(S=5000) == E.E0_ERR_CAPACITY
+    assert call(ws_bytes=8) == E.E0_ERR_CAPACITY
+    assert call(nxt=None) == E.E0_ERR_INVALID_ARG
+    assert call(store=_stack(FAKE + 8)) == E.E0_ERR_INVALID_ARG
+    assert call(dims=E.moe_dims(2048, 500, 256, 4)) == E.E0_ERR_UNSUPPORTED_SHAPE
+
+
+def test_prerouter_validation():
+    heads = E.PrerouterHeads(FAKE, 0, None, 0, FAKE, 0, None, 0, FAKE, 0, 512, 0)
+    L = E.lib()
+
+    def call(heads=heads, B=1, d=2048, Ex=256, ws_bytes=1 << 24, p=E.route_params(0, 4)):
+        return L.e0_prerouter(C.byref(heads), 32, B, d, Ex, C.c_void_p(FAKE), C.c_void_p(FAKE), None, C.byref(p),
+                              C.c_void_p(FAKE), C.c_void_p(FAKE), None, C.c_void_p(FAKE), ws_bytes, None)
+    assert call(B=65) == E.E0_ERR_CAPACITY
+    assert call(d=100) == E.E0_ERR_UNSUPPORTED_SHAPE
+    assert call(ws_bytes=16) == E.E0_ERR_CAPACITY
+    bad = E.PrerouterHeads(FAKE, 0, None, 0, FAKE, 0, None, 0, FAKE, 0, 100, 0)
+    assert call(heads=bad) == E.E0_ERR_UNSUPPORTED_SHAPE
+    assert call(p=E.route_params(0, 300)) == E.E0_ERR_UNSUPPORTED_SHAPE
+
+
+def test_prefill_validation():
+    L = E.lib()
+    st = _stack()
+    dims = E.moe_dims(2048, 100, 256, 4)
+    rc = L.e0_moe_sorted_prefill(C.byref(dims), 16, C.c_void_p(FAKE), C.c_void_p(FAKE), C.c_void_p(FAKE),
+                                 C.byref(st), C.c_void_p(FAKE), C.c_void_p(FAKE), 1 << 20, C.c_void_p(FAKE), None)
+    assert rc == E.E0_ERR_UNSUPPORTED_SHAPE
+
+
+def test_binding_has_no_fallback(monkeypatch, tmp_path):
+    monkeypatch.setattr(E, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(E, "_LIB", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        E.lib()
