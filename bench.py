@@ -34,6 +34,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true", help="run the slot update on the decode stream")
     ap.add_argument("--cpu-steps", type=int, default=0, help="oracle steps in the CPU baseline (0 = auto)")
     return ap.parse_args()
 
@@ -71,7 +72,7 @@ def main():
     dims = E.moe_dims(d, f, Ex, K)
     st_store = E.stack_from_bundles(store, d, f, bb, Ex * bb)
     st_pool = E.stack_from_bundles(pool, d, f, bb, S * bb)
-    pipe = StagedPipeline(dims, L, B, S, st_store, st_pool, device=dev)
+    pipe = StagedPipeline(dims, L, B, S, st_store, st_pool, device=dev, side_stream=not args.no_overlap)
     rp = E.route_params(0, K)
 
     ev_dec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -85,10 +86,11 @@ def main():
 
     def step(t, rec=None):
         nb, cb = (t + 1) % 2, t % 2
-        pipe.route_given(nb, rp, logits[(t + 1) % n_in])
+        pipe.side_after_main()
         if rec is not None:
             ev_upd[rec][0].record(pipe.side)
-        pipe.update(nb, cb)
+        pipe.route_given(nb, rp, logits[(t + 1) % n_in], on_side=True)
+        pipe.update(nb, cb, after_main=False)
         if rec is not None:
             ev_upd[rec][1].record(pipe.side)
             ev_dec[rec][0].record(pipe.main)
@@ -138,8 +140,9 @@ def main():
                    "layers": L, "experts": Ex, "d_model": d, "d_ff": f, "top_k": K, "batch": B, "slots": S},
         "layer_tok_per_s": round(args.steps * B * L / wall, 1),
         "decode_call_us": round(dec_ms * 1e3, 2),
-        "slot_update_us": round(upd_ms * 1e3, 2),
+        "route_and_slot_update_us": round(upd_ms * 1e3, 2),
         "slot_copies_last_step": copies,
+        "overlap": not args.no_overlap,
         "roofline": {"bound": "hbm", "kernel": "e0_moe_staged_decode (gate/up + down launches)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,

@@ -87,7 +87,7 @@ E0_DEV float silu(float z) { return z / (1.0f + expf(-z)); }
 // Block-wide exclusive scan of one int per thread (256 threads).
 // ---------------------------------------------------------------------------
 E0_DEV int block_exclusive_scan(int v, int *lds4, int &total) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
     int inc = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -239,19 +239,40 @@ E0_DEV void x_pairs(const u32x4 v, uint32_t (&o)[4]) {
     o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
 }
 
-// sum over the 8 codes of `w` of (16 + q_c) * x_c, x given as pairs.
-E0_DEV float dot_word(uint32_t w, const uint32_t (&xp)[4], float acc) {
-    const uint32_t m = 0x03C003C0u, one6 = 0x4C004C00u;
-    const uint32_t t0 = ((w << 6) & m) | one6;
-    const uint32_t t1 = ((w << 2) & m) | one6;
-    const uint32_t t2 = ((w >> 2) & m) | one6;
-    const uint32_t t3 = ((w >> 6) & m) | one6;
+// (a & m) | c in one v_and_or_b32. gfx9 VOP3 instructions take at most one
+// scalar or literal operand, so the two constants live in VGPRs (held by the
+// caller) and the instruction is spelled out.
+E0_DEV uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+    uint32_t r;
+    __asm__("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+    return r;
+}
+
+// Constants of the nibble-to-fp16 placement, kept in VGPRs.
+struct NibbleConsts {
+    uint32_t mask, one6;
+};
+E0_DEV NibbleConsts nibble_consts() {
+    NibbleConsts k;
+    __asm__("v_mov_b32 %0, 0x03c003c0" : "=v"(k.mask));
+    __asm__("v_mov_b32 %0, 0x4c004c00" : "=v"(k.one6));
+    return k;
+}
+
+// sum over the 8 codes of `w` of (16 + q_c) * x_c, x given as pairs
+// (x_j, x_{j+4}); code pair (q_j, q_{j+4}) lands at bits 6..9 of each half.
+E0_DEV float dot_word(uint32_t w, const uint32_t (&xp)[4], float acc, NibbleConsts k) {
+    const uint32_t t0 = and_or(w << 6, k.mask, k.one6);
+    const uint32_t t1 = and_or(w << 2, k.mask, k.one6);
+    const uint32_t t2 = and_or(w >> 2, k.mask, k.one6);
+    const uint32_t t3 = and_or(w >> 6, k.mask, k.one6);
     acc = __builtin_amdgcn_fdot2(as_h2(t0), as_h2(xp[0]), acc, false);
     acc = __builtin_amdgcn_fdot2(as_h2(t1), as_h2(xp[1]), acc, false);
     acc = __builtin_amdgcn_fdot2(as_h2(t2), as_h2(xp[2]), acc, false);
     acc = __builtin_amdgcn_fdot2(as_h2(t3), as_h2(xp[3]), acc, false);
     return acc;
 }
+E0_DEV float dot_word(uint32_t w, const uint32_t (&xp)[4], float acc) { return dot_word(w, xp, acc, nibble_consts()); }
 
 // ---------------------------------------------------------------------------
 // 2. gateup. Template: LPR lanes per row pass (d = 32 * LPR * NP), TC tokens
@@ -263,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
     constexpr int ROWS_W = RPI * RB;          // rows per wave
     constexpr int ROWS_B = ROWS_W * kWaves;   // rows per block
     constexpr int NV = 2 * RB * TC;           // partial values per lane
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
     const int gl = lane % LPR, grp = lane / LPR;
     const int l = blockIdx.x, u = blockIdx.y;
     const bool is_shared = a.has_shared && u == a.umax;
@@ -464,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(DecodeArgs a) {
     constexpr int IT = DownCfg<LPR>::IT;
     __shared__ float s_acc[kMaxB][kDownRows];
     __shared__ float s_lora[kMaxB][kMaxR];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
     const int gl = lane % LPR, grp = lane / LPR;
     const int l = blockIdx.x;
     const int row0 = blockIdx.y * kDownRows;
@@ -595,6 +616,234 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(DecodeArgs a) {
             v += a.lscale * dl;
         }
         a.y[((int64_t)l * a.B + t) * d + row] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Batch-1 flat kernels. The rows of all experts of all layers form one list
+// (layer, expert u, row), u = 0..K-1 the routed experts of the token and u = K
+// the shared expert; each wavefront takes kFlatRows consecutive rows, which
+// never straddle an expert (kFlatRows divides d_ff) so x and the expert's
+// buffer descriptors are set once per wave. The grid is one round of resident
+// waves: no tail of half-empty rounds, no per-block imbalance.
+// ---------------------------------------------------------------------------
+constexpr int kFlatRows = 32;  // rows per wavefront
+constexpr int kFlatBatch = 4;  // rows per pipeline stage (loads issued together)
+
+// Resolve expert u of layer l (batch 1): its slot (shared expert: slot 0 of
+// the shared stack), or false for an invalid / non-resident id.
+E0_DEV bool resolve_b1(const DecodeArgs &a, int l, int u, int &slot, bool flag) {
+    if (u == a.K) {
+        slot = 0;
+        return true;
+    }
+    const int e = a.idx[(int64_t)l * a.K + u];
+    if (e < 0 || e >= a.E) {
+        if (flag) set_err(a.err, E0_DEV_BAD_ID);
+        return false;
+    }
+    slot = a.slot_of[(int64_t)l * a.E + e];
+    if (slot < 0 || slot >= a.S) {
+        if (flag) set_err(a.err, E0_DEV_NOT_RESIDENT);
+        return false;
+    }
+    return true;
+}
+
+// Part i of expert u's stack, by value (selecting a pointer between two
+// kernel-argument structs would put the arguments in private memory).
+E0_DEV Part part_of(const DecodeArgs &a, int u, int i) { return u == a.K ? a.sh.p[i] : a.pool.p[i]; }
+
+template <int NP>
+__global__ __launch_bounds__(kThreads) void decode_gateup_flat_kernel(DecodeArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int U = a.K + (a.has_shared ? 1 : 0);
+    const int64_t r0 = ((int64_t)blockIdx.x * kWaves + wave_id()) * kFlatRows;
+    if (r0 >= (int64_t)a.L * U * a.f) return;
+    const int l = (int)(r0 / ((int64_t)U * a.f));
+    const int u = (int)((r0 / a.f) % U);
+    const int row0 = (int)(r0 % a.f);
+    int slot;
+    if (!resolve_b1(a, l, u, slot, row0 == 0 && lane == 0)) return;
+    const int d = a.d, ngrp = d / kGroup;
+
+    // x of this layer: 32 inputs per lane per pass, as (x_j, x_{j+4}) pairs.
+    uint32_t xp[NP][4][4];
+    float xs[NP];
+#pragma unroll
+    for (int np = 0; np < NP; ++np) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(a.x + (int64_t)l * d + (np * 64 + lane) * 32 + wd * 8);
+            x_pairs(v, xp[np][wd]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f16x2 hv = as_h2(v[j]);
+                sum += (float)hv[0] + (float)hv[1];
+            }
+        }
+        xs[np] = sum;
+    }
+    rsrc_t qr[2], sr[2], br[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        qr[m] = make_rsrc(part_at(part_of(a, u, 3 * m + 0), l, slot), (uint32_t)a.f * d / 2);
+        sr[m] = make_rsrc(part_at(part_of(a, u, 3 * m + 1), l, slot), (uint32_t)a.f * ngrp * 2);
+        br[m] = make_rsrc(part_at(part_of(a, u, 3 * m + 2), l, slot), (uint32_t)a.f * ngrp * 2);
+    }
+    float *hout = hrow(a, l, u);
+    const bool lora = u == a.K && a.r > 0;
+    const NibbleConsts nk = nibble_consts();
+
+    // Two-stage software pipeline over batches of kFlatBatch rows: the loads
+    // of batch b+1 are in flight while batch b is computed. The memory
+    // clobbers keep the compiler from hoisting later batches' loads.
+    struct Batch {
+        u32x4 q[kFlatBatch][2][NP];
+        uint32_t sb[kFlatBatch][2][NP];  // fp16 scale | fp16 bias << 16
+    };
+    auto load = [&](int b0, Batch &B) {
+#pragma unroll
+        for (int rr = 0; rr < kFlatBatch; ++rr) {
+            const uint32_t row = (uint32_t)(row0 + b0 + rr);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                for (int np = 0; np < NP; ++np) {
+                    const uint32_t col = (uint32_t)(np * 64 + lane);
+                    B.q[rr][m][np] = ld128(qr[m], row * (d / 2) + col * 16);
+                    const uint32_t so = (row * ngrp + col / 2) * 2;
+                    B.sb[rr][m][np] = (uint32_t)ld16(sr[m], so) | ((uint32_t)ld16(br[m], so) << 16);
+                }
+            }
+        }
+    };
+    auto compute = [&](int b0, const Batch &B) {
+        float acc[2 * kFlatBatch];
+#pragma unroll
+        for (int rr = 0; rr < kFlatBatch; ++rr) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                float v = 0.0f;
+#pragma unroll
+                for (int np = 0; np < NP; ++np) {
+                    float dacc = 0.0f;
+#pragma unroll
+                    for (int wd = 0; wd < 4; ++wd) dacc = dot_word(B.q[rr][m][np][wd], xp[np][wd], dacc, nk);
+                    const f16x2 sbv = as_h2(B.sb[rr][m][np]);
+                    const float sc = (float)sbv[0], bi = (float)sbv[1];
+                    v += sc * dacc + (bi - 16.0f * sc) * xs[np];
+                }
+                acc[m * kFlatBatch + rr] = v;
+            }
+        }
+        // 2*kFlatBatch values over 64 lanes; gate values in lanes 0..31, the
+        // matching up value in lane ^ 32.
+        group_reduce_scatter<2 * kFlatBatch, kWave>(acc);
+        constexpr int DUP = kWave / (2 * kFlatBatch);
+        const int vi = lane / DUP, m = vi / kFlatBatch, rr = vi % kFlatBatch;
+        const int row = row0 + b0 + rr;
+        float val = acc[0];
+        if (lora) {
+            const uint16_t *brow = a.lb[m] + (int64_t)l * (a.lb_ls[m] / 2) + (int64_t)row * a.r;
+            const float *av = a.lora_a + ((int64_t)l * 3 + m) * a.r;
+            float dl = 0.0f;
+            for (int i = 0; i < a.r; ++i) dl += h2f(brow[i]) * av[i];
+            val += a.lscale * dl;
+        }
+        const float other = __shfl_xor(val, 32);
+        if (m == 0 && lane % DUP == 0) hout[row] = silu(val) * other;
+    };
+
+    Batch B0, B1;
+    load(0, B0);
+#pragma unroll
+    for (int b0 = 0; b0 < kFlatRows; b0 += 2 * kFlatBatch) {
+        if (b0 + kFlatBatch < kFlatRows) load(b0 + kFlatBatch, B1);
+        __asm__ __volatile__("" ::: "memory");
+        compute(b0, B0);
+        __asm__ __volatile__("" ::: "memory");
+        if (b0 + 2 * kFlatBatch < kFlatRows) load(b0 + 2 * kFlatBatch, B0);
+        __asm__ __volatile__("" ::: "memory");
+        if (b0 + kFlatBatch < kFlatRows) compute(b0 + kFlatBatch, B1);
+        __asm__ __volatile__("" ::: "memory");
+    }
+}
+
+template <int LPR>
+__global__ __launch_bounds__(kThreads) void decode_down_flat_kernel(DecodeArgs a) {
+    constexpr int RPI = kWave / LPR;        // rows per wave instruction
+    constexpr int IT = kFlatRows / RPI;     // instructions per wave
+    __shared__ float s_lora[kMaxR];
+    const int lane = threadIdx.x & 63, wv = wave_id();
+    const int gl = lane % LPR, grp = lane / LPR;
+    const int f = a.f, d = a.d, fgrp = f / kGroup;
+    // A block covers kWaves * kFlatRows rows of one layer (d is a multiple of 128).
+    const int64_t rb0 = (int64_t)blockIdx.x * kWaves * kFlatRows;
+    if (rb0 >= (int64_t)a.L * d) return;
+    const int l = (int)(rb0 / d);
+    const int row0 = (int)(rb0 % d) + wv * kFlatRows;
+    const bool lora = a.has_shared && a.r > 0;
+    if (lora) {
+        // a_d = A_down h_shared for this layer, once per block.
+        const float *hs = hrow(a, l, a.K);
+        for (int i = wv; i < a.r; i += kWaves) {
+            const uint16_t *arow = a.la[2] + (int64_t)l * (a.la_ls[2] / 2) + (int64_t)i * f;
+            float acc = 0.0f;
+            for (int c = lane; c < f; c += kWave) acc += h2f(arow[c]) * hs[c];
+            acc = wave_sum(acc);
+            if (lane == 0) s_lora[i] = acc;
+        }
+        __syncthreads();
+    }
+    const int col0 = gl * 32, g = col0 / kGroup;
+    float acc[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) acc[it] = 0.0f;
+    const int U = a.K + (a.has_shared ? 1 : 0);
+    for (int u = 0; u < U; ++u) {
+        int slot;
+        if (!resolve_b1(a, l, u, slot, false)) continue;
+        const float wk = u < a.K ? a.w[(int64_t)l * a.K + u] : 1.0f;
+        const rsrc_t qb = make_rsrc(part_at(part_of(a, u, 6), l, slot), (uint32_t)d * f / 2);
+        const rsrc_t sb = make_rsrc(part_at(part_of(a, u, 7), l, slot), (uint32_t)d * fgrp * 2);
+        const rsrc_t bb = make_rsrc(part_at(part_of(a, u, 8), l, slot), (uint32_t)d * fgrp * 2);
+        u32x4 qv[IT];
+        float sv[IT], bv[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const uint32_t row = (uint32_t)(row0 + it * RPI + grp);
+            qv[it] = ld128(qb, row * (f / 2) + gl * 16);
+            sv[it] = h2f(ld16(sb, (row * fgrp + g) * 2));
+            bv[it] = h2f(ld16(bb, (row * fgrp + g) * 2));
+        }
+        const float *hp = hrow(a, l, u) + col0;
+        float h[32];
+        float hsum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(hp + 4 * i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                h[4 * i + j] = v[j];
+                hsum += v[j];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) acc[it] += wk * down_dot(qv[it], sv[it], bv[it], h, hsum);
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        float v = group_sum(acc[it], LPR);
+        const int row = row0 + it * RPI + grp;
+        if (lora) {
+            const uint16_t *brow = a.lb[2] + (int64_t)l * (a.lb_ls[2] / 2) + (int64_t)row * a.r;
+            float dl = 0.0f;
+            for (int i = 0; i < a.r; ++i) dl += h2f(brow[i]) * s_lora[i];
+            v += a.lscale * dl;
+        }
+        if (gl == 0) a.y[(int64_t)l * d + row] = v;
     }
 }
 
@@ -775,6 +1024,29 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
     if (a.has_plan || (a.has_shared && r > 0)) {
         hipLaunchKernelGGL(decode_prep_kernel, dim3(L), dim3(kThreads), 0, st, a);
         if ((s = e0_launch_status())) return s;
+    }
+    if (B == 1 && lpr_d == 64) {
+        // Batch 1 at d_model = 2048 * NP: the flat one-round kernels.
+        const int U = K + (a.has_shared ? 1 : 0);
+        const int64_t gu_waves = ((int64_t)L * U * f) / kFlatRows;
+        const int64_t dn_waves = ((int64_t)L * d) / kFlatRows;
+        E0_REQUIRE(gu_waves <= (int64_t)INT32_MAX && dn_waves <= (int64_t)INT32_MAX, E0_ERR_CAPACITY);
+        const dim3 gu_grid((unsigned)((gu_waves + kWaves - 1) / kWaves)), dn_grid((unsigned)((dn_waves + kWaves - 1) / kWaves));
+        switch (np) {
+            case 1: hipLaunchKernelGGL(decode_gateup_flat_kernel<1>, gu_grid, dim3(kThreads), 0, st, a); break;
+            case 2: hipLaunchKernelGGL(decode_gateup_flat_kernel<2>, gu_grid, dim3(kThreads), 0, st, a); break;
+            case 3: hipLaunchKernelGGL(decode_gateup_flat_kernel<3>, gu_grid, dim3(kThreads), 0, st, a); break;
+            default: hipLaunchKernelGGL(decode_gateup_flat_kernel<4>, gu_grid, dim3(kThreads), 0, st, a); break;
+        }
+        if ((s = e0_launch_status())) return s;
+        switch (lpr_f) {
+            case 4: hipLaunchKernelGGL(decode_down_flat_kernel<4>, dn_grid, dim3(kThreads), 0, st, a); break;
+            case 8: hipLaunchKernelGGL(decode_down_flat_kernel<8>, dn_grid, dim3(kThreads), 0, st, a); break;
+            case 16: hipLaunchKernelGGL(decode_down_flat_kernel<16>, dn_grid, dim3(kThreads), 0, st, a); break;
+            case 32: hipLaunchKernelGGL(decode_down_flat_kernel<32>, dn_grid, dim3(kThreads), 0, st, a); break;
+            default: hipLaunchKernelGGL(decode_down_flat_kernel<64>, dn_grid, dim3(kThreads), 0, st, a); break;
+        }
+        return e0_launch_status();
     }
     const int ublocks = a.umax + (a.has_shared ? 1 : 0);
     if (B == 1) {

@@ -14,6 +14,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+
+// Index of this wavefront in its workgroup, as a wave-uniform (scalar) value:
+// derived values stay in SGPRs and buffer descriptors built from them need no
+// per-lane waterfall loops.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 constexpr int kGroup = 64;  // quantisation group along the input dimension
 
 // A part of a stacked tensor, as kernels see it.

@@ -59,7 +59,7 @@ E0_DEV float gelu_erf(float a) { return 0.5f * a * (1.0f + erff(a * 0.7071067811
 __global__ __launch_bounds__(kWave *kWaves) void prer_fc1_kernel(PrerArgs a) {
     const int lane = threadIdx.x & 63;
     const int j = blockIdx.y;
-    const int r = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int r = blockIdx.x * kWaves + wave_id();
     if (r >= a.hid + a.E) return;
     const bool is_fc1 = r < a.hid;
     const int din = a.d + 2 * a.E;
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kWave *kWaves) void prer_fc1_kernel(PrerArgs a) {
 __global__ __launch_bounds__(kWave *kWaves) void prer_fc2_kernel(PrerArgs a) {
     const int lane = threadIdx.x & 63;
     const int j = blockIdx.y;
-    const int e = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int e = blockIdx.x * kWaves + wave_id();
     if (e >= a.E) return;
     const uint16_t *row = reinterpret_cast<const uint16_t *>(a.fc2_w + (int64_t)j * a.fc2_ws) + (int64_t)e * a.hid;
     const float bias = a.fc2_b ? h2f(reinterpret_cast<const uint16_t *>(a.fc2_b + (int64_t)j * a.fc2_bs)[e]) : 0.0f;

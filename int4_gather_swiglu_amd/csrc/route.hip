@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kWave *kRouteWaves) void route_select_kernel(RouteA
     __shared__ float lds_l[kRouteWaves][kMaxE];
     __shared__ float lds_gs[kRouteWaves][kWave];
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = wave_id();
     const int row = blockIdx.x * kRouteWaves + wv;
     if (row >= a.rows) return;
     const int E = a.E, K = a.K;
@@ -168,7 +168,7 @@ struct GemvArgs {
 
 __global__ __launch_bounds__(kWave *kGemvWaves) void router_gemv_kernel(GemvArgs a) {
     const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * kGemvWaves + (threadIdx.x >> 6);
+    const int e = blockIdx.x * kGemvWaves + wave_id();
     const int l = blockIdx.y;
     if (e >= a.E) return;
     // chunk c covers elements [512c, 512c + 512): 8 halves per lane

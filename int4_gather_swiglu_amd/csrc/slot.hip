@@ -42,7 +42,7 @@ struct SlotArgs {
 
 // Exclusive scan of one int per thread over the block.
 E0_DEV int block_scan(int v, int *lds, int &total) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = wave_id();
     int inc = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {

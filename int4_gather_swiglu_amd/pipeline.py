@@ -5,8 +5,9 @@ Per step t (fixed double-buffered slots, routing ids kept on the GPU; the
 update for step t+1 overlaps step t: koala.ai.kr paths table and Fig. 1
 timeline; jaehun.me review, report 3.1):
 
-  main : routing of step t+1          -> idx[(t+1) % 2]   (e0_route or e0_prerouter)
-  side : (waits for it) slot update   next = idx[(t+1) % 2], in use = idx[t % 2]
+  side : waits for the work already on main (decode t-1 read idx[(t+1) % 2])
+  side : routing of step t+1          -> idx[(t+1) % 2]   (e0_route)
+  side : slot update                  next = idx[(t+1) % 2], in use = idx[t % 2]
   main : staged decode of step t      reads idx[t % 2] through the slot table
   main : (before step t+1) waits for the side stream
 
@@ -46,20 +47,26 @@ class StagedPipeline:
         self.ev_updated = torch.cuda.Event()
 
     # -- pieces -------------------------------------------------------------
-    def route_given(self, buf: int, params: E.RouteParams, logits, fp16: bool = True):
+    def side_after_main(self):
+        """Make the side stream wait for everything enqueued on main so far."""
+        self.ev_routed.record(self.main)
+        self.side.wait_event(self.ev_routed)
+
+    def route_given(self, buf: int, params: E.RouteParams, logits, fp16: bool = True, on_side: bool = False):
         """Route step logits [L][B][E] (fp16 bits or fp32) into idx/w[buf]."""
         E.e0_route(params, self.L, self.B, self.dims.n_experts, logits, fp16, None, None, 0, self.idx[buf],
-                   self.w[buf], None, stream=self.main)
+                   self.w[buf], None, stream=self.side if on_side else self.main)
 
     def route_router(self, buf: int, params: E.RouteParams, x, w_router, logits_out):
         """Route with each layer's own router over x [L][B][d]."""
         E.e0_route(params, self.L, self.B, self.dims.n_experts, None, False, x, w_router, self.dims.d_model,
                    self.idx[buf], self.w[buf], logits_out, stream=self.main)
 
-    def update(self, nxt: int, cur: int | None):
-        """Slot update for idx[nxt], protecting idx[cur], on the side stream."""
-        self.ev_routed.record(self.main)
-        self.side.wait_event(self.ev_routed)
+    def update(self, nxt: int, cur: int | None, after_main: bool = True):
+        """Slot update for idx[nxt], protecting idx[cur], on the side stream
+        (after the work on main unless after_main is False)."""
+        if after_main:
+            self.side_after_main()
         E.e0_slot_update(self.dims, self.L, self.B, self.S, self.idx[nxt], None if cur is None else self.idx[cur],
                          self.slot_of, self.expert_of, self.store, self.pool, self.n_copied, self.ws_slot, self.err,
                          stream=self.side)
