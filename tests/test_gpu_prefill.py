@@ -1,0 +1,128 @@
+"""GPU parity: sorted whole-layer prefill (sort by expert, MFMA grouped GEMM,
+weighted combine) against the fp64 oracle, rel-L2 <= 1e-3. fp16 MFMA
+operands (x exact; weights and the SwiGLU hidden rounded to fp16) put the
+expected error near 3e-4."""
+import numpy as np
+import pytest
+
+import oracle
+from e0inputs import gen, workloads as W
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+
+
+def E():
+    from int4_gather_swiglu_amd import _lib
+    return _lib
+
+
+def _prefill(cfg, store_layer, x, idx, w):
+    """Run e0_moe_sorted_prefill on device tensors; returns y (host) and err."""
+    T = x.shape[0]
+    bb = gen.bundle_bytes(cfg.d, cfg.f)
+    dims = E().moe_dims(cfg.d, cfg.f, cfg.E, idx.shape[1])
+    st = E().stack_from_bundles(store_layer, cfg.d, cfg.f, bb, 0)
+    ws = U.empty((E().workspace_bytes(E().E0_OP_SORTED_PREFILL, dims, T),), "uint8")
+    y = U.empty((T, cfg.d))
+    err = U.zeros((1,), "int32")
+    E().e0_moe_sorted_prefill(dims, T, U.f16(x), U.i32(idx), U.f32(w), st, y, ws, err)
+    U.torch().cuda.synchronize()
+    return y.cpu().numpy(), int(err.item())
+
+
+def _oracle(cfg, layer, x, idx, w, tokens):
+    ids = sorted(set(idx[tokens].ravel().tolist()) - {-1})
+    mats = {e: gen.expert(cfg.seed, layer, e, cfg.d, cfg.f) for e in ids if 0 <= e < cfg.E}
+    first = next(iter(mats.values()))
+    lst = [mats.get(e, first) for e in range(cfg.E)]
+    idx_s = idx[tokens].copy()
+    w_s = w[tokens].astype(np.float64)
+    bad = (idx_s < 0) | (idx_s >= cfg.E)
+    idx_s[bad] = ids[0]
+    w_s[bad] = 0.0
+    ref, _ = oracle.moe_exact(oracle.Experts(lst), cfg.d, cfg.f, x[tokens], idx_s, w_s)
+    return ref
+
+
+def test_tiny_prefill_all_tokens():
+    cfg = W.scaled(W.TINY, B=37)
+    store = U.gpu_store(cfg, [0])[0]
+    x = W.activations(cfg, 0, 0)
+    lg = W.given_logits(cfg, 0, 0).astype(np.float32)
+    idx, w = oracle.softmax_topk(lg, cfg.K)
+    y, err = _prefill(cfg, store, x, idx, w.astype(np.float32))
+    assert err == 0
+    ref = _oracle(cfg, 0, x, idx, w.astype(np.float32), np.arange(cfg.B))
+    r = U.rel_l2(y, ref)
+    print("tiny prefill rel-L2", r)
+    assert r <= TOL
+
+
+@pytest.mark.parametrize("T", [1, 5, 128, 300])
+def test_tiny_prefill_ragged_and_single_token(T):
+    cfg = W.scaled(W.TINY, B=T)
+    store = U.gpu_store(cfg, [0])[0]
+    x = W.activations(cfg, 1, 0)
+    idx, w = oracle.softmax_topk(W.given_logits(cfg, 1, 0).astype(np.float32), cfg.K)
+    y, err = _prefill(cfg, store, x, idx, w.astype(np.float32))
+    assert err == 0
+    tok = np.unique(np.linspace(0, T - 1, min(T, 24)).astype(int))
+    assert U.rel_l2(y[tok], _oracle(cfg, 0, x, idx, w.astype(np.float32), tok)) <= TOL
+
+
+def test_prefill_one_expert_takes_every_token():
+    cfg = W.scaled(W.TINY, B=300)
+    store = U.gpu_store(cfg, [0])[0]
+    x = W.activations(cfg, 2, 0)
+    idx = np.tile(np.array([[5, 2, 9, 0]], np.int32), (cfg.B, 1))
+    idx[::3, 1] = 7  # a second popular expert on a third of the tokens
+    w = np.tile(np.array([[0.4, 0.3, 0.2, 0.1]], np.float32), (cfg.B, 1))
+    y, err = _prefill(cfg, store, x, idx, w)
+    assert err == 0
+    tok = np.arange(0, cfg.B, 13)
+    assert U.rel_l2(y[tok], _oracle(cfg, 0, x, idx, w, tok)) <= TOL
+
+
+def test_prefill_bad_ids_flag_and_skip():
+    cfg = W.scaled(W.TINY, B=16)
+    store = U.gpu_store(cfg, [0])[0]
+    x = W.activations(cfg, 3, 0)
+    idx, w = oracle.softmax_topk(W.given_logits(cfg, 3, 0).astype(np.float32), cfg.K)
+    idx[3, 2] = cfg.E
+    idx[7, 0] = -1
+    w = w.astype(np.float32)
+    y, err = _prefill(cfg, store, x, idx, w)
+    assert err == E().E0_DEV_BAD_ID
+    assert U.rel_l2(y, _oracle(cfg, 0, x, idx, w, np.arange(cfg.B))) <= TOL
+
+
+def test_prefill35b_zipf_full_shape_sampled():
+    cfg = W.PREFILL35
+    T = cfg.B
+    store = U.gpu_store(cfg, [0])[0]
+    x = W.activations(cfg, 0, 0)
+    lg16 = W.given_logits(cfg, 0, 0)
+    # routing on the GPU (as the bench does), checked against the oracle
+    p = E().route_params(0, cfg.K)
+    idx_d = U.empty((1, T, cfg.K), "int32")
+    w_d = U.empty((1, T, cfg.K))
+    E().e0_route(p, 1, T, cfg.E, U.f16(lg16[None]), True, None, None, 0, idx_d, w_d, None)
+    U.torch().cuda.synchronize()
+    idx = idx_d.cpu().numpy()[0]
+    w = w_d.cpu().numpy()[0]
+    ridx, rw = oracle.softmax_topk(lg16.astype(np.float32), cfg.K)
+    assert np.array_equal(idx, ridx)
+    counts = np.bincount(idx.ravel(), minlength=cfg.E)
+    print("active experts", int((counts > 0).sum()), "top count", int(counts.max()),
+          "experts < 16 rows", int(((counts > 0) & (counts < 16)).sum()))
+    y, err = _prefill(cfg, store, x, idx, w)
+    assert err == 0
+    top = int(np.argmax(counts))
+    tok_top = np.nonzero((idx == top).any(1))[0][:6]
+    tok_rare = [int(np.nonzero((idx == e).any(1))[0][0]) for e in np.nonzero((counts > 0) & (counts < 4))[0][:6]]
+    tok = np.unique(np.concatenate([tok_top, tok_rare, [0, T - 1]])).astype(int)
+    r = U.rel_l2(y[tok], _oracle(cfg, 0, x, idx, w, tok))
+    print("prefill35b rel-L2 on", len(tok), "tokens:", r)
+    assert r <= TOL
