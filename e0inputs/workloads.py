@@ -221,3 +221,59 @@ def head_weight_bytes(cfg: Config) -> int:
 def gib(x: float) -> float:
     return x / float(1 << 30)
 
+
+
+# ---------------------------------------------------------------------------
+# Prerouted pipeline inputs (32 staged layers, one head per staged layer)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Prerouted:
+    """Per-step inputs of the prerouted pipeline.
+
+    hin[t]    fp16 [L+1][d]: row 0 is the hidden of the unstaged layer that
+              owns head 0; row 1 + l is the MoE input of staged layer l at
+              step t. Head j reads row j (its owner's hidden: staged layer
+              j-1, or the unstaged owner for j = 0); the decode reads rows
+              1..L. Rows 0..L-1 are planted for the targets of step t+1; row L
+              (the last staged layer, whose head has no staged consumer) is
+              N(0,1).
+    owner0[t] int32 [K]: routing of the unstaged owner at step t (p-repeat process).
+    r0        int32 [L][K]: routing of the staged layers at step 0.
+    targets[t] int32 [L][K]: the sets planted for step t+1.
+    """
+    hin: np.ndarray
+    owner0: np.ndarray
+    r0: np.ndarray
+    targets: np.ndarray
+
+
+def prerouted_inputs(cfg: Config, steps: int, accept=None) -> Prerouted:
+    """Draw the prerouted pipeline's inputs for `steps` steps.
+
+    accept(t, j, h) -> bool, if given, may reject a planted hidden (the caller
+    decides, e.g. on a decision margin); it is then redrawn with the next
+    attempt number."""
+    L, K = cfg.L, cfg.K
+    planters = [Planter(router_weights(cfg, j)) for j in range(L)]
+    r0 = np.stack([initial_set(cfg, l) for l in range(L)])
+    owner0 = np.empty((steps, K), np.int32)
+    owner0[0] = initial_set(cfg, -1)
+    for t in range(1, steps):
+        owner0[t] = next_set(cfg, owner0[t - 1], t, -1)
+    targets = np.empty((steps, L, K), np.int32)
+    cur = r0.copy()
+    hin = np.empty((steps, L + 1, cfg.d), np.float16)
+    for t in range(steps):
+        for j in range(L):
+            tgt = next_set(cfg, cur[j], t + 1, j)
+            targets[t, j] = tgt
+            att = 0
+            h = planters[j].hidden(cfg, tgt, t, j, att)
+            while accept is not None and not accept(t, j, h):
+                att += 1
+                h = planters[j].hidden(cfg, tgt, t, j, att)
+            hin[t, j] = h
+        hin[t, L] = activations(cfg, t, L - 1)[0]
+        cur = targets[t]
+    return Prerouted(hin=hin, owner0=owner0, r0=r0, targets=targets)

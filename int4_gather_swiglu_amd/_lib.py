@@ -190,3 +190,31 @@ def e0_slot_update(dims: MoeDims, L: int, B: int, S: int, next_idx, cur_idx, slo
                                 _ptr(expert_of), C.byref(store), C.byref(pool), _ptr(n_copied), _ptr(ws),
                                 ws.numel() * ws.element_size() if ws is not None else 0, _ptr(dev_err),
                                 _stream(stream)), "e0_slot_update")
+
+
+def heads_from_tensors(fc1_w, fc1_b, fc2_w, fc2_b, lin_w) -> PrerouterHeads:
+    """e0_prerouter_heads over stacked per-head fp16 tensors:
+    fc1_w [H][hid][d+2E], fc1_b [H][hid] or None, fc2_w [H][E][hid],
+    fc2_b [H][E] or None, lin_w [H][E][d]."""
+    def ps(t):
+        return (t.data_ptr(), t[0].numel() * t.element_size()) if t is not None else (None, 0)
+    (a, sa), (b, sb), (c, sc), (d_, sd), (e, se) = ps(fc1_w), ps(fc1_b), ps(fc2_w), ps(fc2_b), ps(lin_w)
+    return PrerouterHeads(a, sa, b, sb, c, sc, d_, sd, e, se, int(fc1_w.shape[1]), 0)
+
+
+def shared_from_tensors(store, d: int, f: int, lora_a=None, lora_b=None, lora_scale: float = 0.0) -> Shared:
+    """e0_shared over per-layer bundles store [L][bundle] (one shared expert
+    per layer) and optional LoRA: lora_a[p] [L][r][in_p], lora_b[p] [L][out_p][r]."""
+    sh = Shared()
+    bb = bundle_bytes(d, f)
+    sh.w = stack_from_bundles(store, d, f, bb, store[0].numel() * store.element_size())
+    sh.d_ff = f
+    sh.lora_rank = int(lora_a[0].shape[1]) if lora_a is not None else 0
+    sh.lora_scale = lora_scale
+    if lora_a is not None:
+        for p in range(3):
+            sh.lora_a[p] = lora_a[p].data_ptr()
+            sh.lora_a_layer_stride[p] = lora_a[p][0].numel() * lora_a[p].element_size()
+            sh.lora_b[p] = lora_b[p].data_ptr()
+            sh.lora_b_layer_stride[p] = lora_b[p][0].numel() * lora_b[p].element_size()
+    return sh

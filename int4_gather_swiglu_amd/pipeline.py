@@ -11,6 +11,10 @@ timeline; jaehun.me review, report 3.1):
   main : staged decode of step t      reads idx[t % 2] through the slot table
   main : (before step t+1) waits for the side stream
 
+With the prerouter, the routing of step t+1 is the heads' prediction made at
+step t (one flush for all staged layers, then the slot update; koala.ai.kr
+prerouter section): PrerouterPipeline.
+
 The update only writes slots whose experts are in neither set, and leaves the
 slot-table entries of step t's experts untouched, so it can run while step t
 reads the pool.
@@ -57,24 +61,53 @@ class StagedPipeline:
         E.e0_route(params, self.L, self.B, self.dims.n_experts, logits, fp16, None, None, 0, self.idx[buf],
                    self.w[buf], None, stream=self.side if on_side else self.main)
 
-    def route_router(self, buf: int, params: E.RouteParams, x, w_router, logits_out):
+    def route_router(self, buf: int, params: E.RouteParams, x, w_router, logits_out, on_side: bool = False):
         """Route with each layer's own router over x [L][B][d]."""
         E.e0_route(params, self.L, self.B, self.dims.n_experts, None, False, x, w_router, self.dims.d_model,
-                   self.idx[buf], self.w[buf], logits_out, stream=self.main)
+                   self.idx[buf], self.w[buf], logits_out, stream=self.side if on_side else self.main)
+
+    def update_ids(self, nxt, cur, after_main: bool = True):
+        """Slot update for routing ids `nxt` [L][B][K], protecting `cur` (or None)."""
+        if after_main:
+            self.side_after_main()
+        E.e0_slot_update(self.dims, self.L, self.B, self.S, nxt, cur, self.slot_of, self.expert_of, self.store,
+                         self.pool, self.n_copied, self.ws_slot, self.err, stream=self.side)
+        self.ev_updated.record(self.side)
 
     def update(self, nxt: int, cur: int | None, after_main: bool = True):
         """Slot update for idx[nxt], protecting idx[cur], on the side stream
         (after the work on main unless after_main is False)."""
-        if after_main:
-            self.side_after_main()
-        E.e0_slot_update(self.dims, self.L, self.B, self.S, self.idx[nxt], None if cur is None else self.idx[cur],
-                         self.slot_of, self.expert_of, self.store, self.pool, self.n_copied, self.ws_slot, self.err,
-                         stream=self.side)
-        self.ev_updated.record(self.side)
+        self.update_ids(self.idx[nxt], None if cur is None else self.idx[cur], after_main)
 
     def join(self):
         self.main.wait_event(self.ev_updated)
 
+    def decode_ids(self, idx, w, x, y):
+        E.e0_moe_staged_decode(self.dims, self.L, self.B, x, idx, w, self.slot_of, self.S, self.pool, self.shared, y,
+                               self.ws_dec, self.err, stream=self.main)
+
     def decode(self, buf: int, x, y):
-        E.e0_moe_staged_decode(self.dims, self.L, self.B, x, self.idx[buf], self.w[buf], self.slot_of, self.S,
-                               self.pool, self.shared, y, self.ws_dec, self.err, stream=self.main)
+        self.decode_ids(self.idx[buf], self.w[buf], x, y)
+
+
+class PrerouterPipeline(StagedPipeline):
+    """Staged decode whose routing is the prerouter heads' prediction.
+
+    Routing state R[t] is [L+1][B][K]: row 0 is the unstaged layer owning head
+    0 (given), rows 1..L the staged layers. Head j reads its owner's hidden
+    hin[j] (hin: [L+1][B][d], rows 1..L are also the decode's inputs), the
+    owner's current and previous routing R[t][j], R[t-1][j], and writes
+    R[t+1][j+1]."""
+
+    def __init__(self, dims, L, B, S, store, pool, heads: E.PrerouterHeads, route: E.RouteParams,
+                 shared=None, device="cuda", side_stream: bool = True):
+        super().__init__(dims, L, B, S, store, pool, shared, device, side_stream)
+        self.heads, self.route = heads, route
+        hd = E.moe_dims(dims.d_model, heads.hidden, dims.n_experts, dims.top_k)
+        self.ws_pre = torch.empty(E.workspace_bytes(E.E0_OP_PREROUTER, hd, L, B), dtype=torch.uint8, device=self.dev)
+
+    def predict(self, hin, r_cur, r_prev, r_next, w_next, logits_out=None):
+        """Heads at step t: hin [L+1][B][d], r_cur / r_prev [L+1][B][K] (r_prev
+        may be None) -> r_next[1:], w_next[1:] (the routing of step t+1)."""
+        E.e0_prerouter(self.heads, self.L, self.B, self.dims.d_model, self.dims.n_experts, hin, r_cur, r_prev,
+                       self.route, r_next[1:], w_next[1:], logits_out, self.ws_pre, stream=self.main)
