@@ -1,16 +1,22 @@
 """Benchmark of the routed-expert int4 g64 SwiGLU hot path on one MI355X.
 
-Default workload (the metric's headline configuration): 35B-tier staged
-decode, batch 1, through 40 stacked MoE layers (d_model 2048, d_ff 512,
-256 experts per layer resident as int4 group-64 bundles in HBM, 2 x 4 slots
-per layer), softmax top-4 from fp16 logits. One step = routing of the next
-step, slot update of the changed experts on a side stream, and the staged
-decode of 40 layers for this step (route -> slot update || decode).
+Default workload (the metric's headline configuration, --workload decode35b):
+35B-tier staged decode, batch 1, through 40 stacked MoE layers (d_model 2048,
+d_ff 512, 256 experts per layer resident as int4 group-64 bundles in HBM,
+2 x 4 slots per layer), softmax top-4 from fp16 logits. One step = routing of
+the next step and the slot update of the changed experts on a side stream,
+overlapped with the staged decode of 40 layers for this step.
 
-Prints ONE JSON line. `value` is MoE-stack tokens per second (steps/s at
-batch 1); `roofline` reports the decode call (its two kernels) against HBM
-peak with the algorithmic expert bytes it must read; `cpu_baseline` is the
-CPU oracle on a bounded sample of the same workload.
+Other workloads (--workload): prefill35b (one layer, T = 2048, Zipf(1.1)
+popularity, sorted MFMA prefill), decode8b_b1 / decode8b_b32 (24 layers,
+sigmoid-group from each layer's router), prerouted35b (32 staged layers:
+heads -> slot update || decode with shared expert + LoRA).
+
+Prints ONE JSON line: `value` is tokens per second (MoE stack at the given
+batch for decode; tokens through one layer for prefill); `roofline` is the
+dominant call (decode: HBM, expert bytes it must read; prefill: fp16 MFMA,
+algorithmic flops) timed with HIP events on its own stream inside the timed
+region; `cpu_baseline` is the CPU oracle on a bounded sample of the workload.
 """
 from __future__ import annotations
 
@@ -25,7 +31,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+MFMA_F16_PEAK_TFS = 2500.0  # MI355X dense fp16/bf16 matrix cores
+METRIC = "MoE-layer tok/s + achieved HBM GB/s (decode) / MFMA util (prefill), int4 g64"
 
 
 def parse():
@@ -33,10 +41,332 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode35b",
+                    choices=["decode35b", "prefill35b", "decode8b_b1", "decode8b_b32", "prerouted35b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overlap", action="store_true", help="run the slot update on the decode stream")
-    ap.add_argument("--cpu-steps", type=int, default=0, help="oracle steps in the CPU baseline (0 = auto)")
+    ap.add_argument("--cpu-steps", type=int, default=0, help="oracle sample size (0 = auto)")
     return ap.parse_args()
+
+
+def events(n):
+    import torch
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def mean_ms(evs):
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def host_threads(limit):
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return max(1, min(n, limit))
+
+
+def run_steps(args, step):
+    """Warm-up, then exactly args.steps timed steps bracketed by synchronize."""
+    import torch
+    t = 0
+    for _ in range(args.warmup):
+        step(t, None)
+        t += 1
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(t, i)
+        t += 1
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+# ---------------------------------------------------------------------------
+# staged decode (35B and 8B tiers)
+# ---------------------------------------------------------------------------
+
+def bench_decode(args, cfg, n_in):
+    import torch
+
+    from e0inputs import gen, gpu as G, workloads as W
+    from int4_gather_swiglu_amd import _lib as E
+    from int4_gather_swiglu_amd.pipeline import StagedPipeline
+
+    dev = torch.device("cuda:0")
+    L, B, K, Ex, S, d, f = cfg.L, cfg.B, cfg.K, cfg.E, cfg.S, cfg.d, cfg.f
+    bb = gen.bundle_bytes(d, f)
+    # The full expert store filled on the GPU; per-step inputs drawn on the
+    # host and resident in HBM before the timed region.
+    store = torch.empty((L, Ex, bb), dtype=torch.uint8, device=dev)
+    for l in range(L):
+        G.fill_experts(store[l].data_ptr(), bb, cfg.seed, l, range(Ex), d, f)
+    pool = torch.zeros((L, S, bb), dtype=torch.uint8, device=dev)
+    xs = torch.from_numpy(np.stack([np.stack([W.activations(cfg, t, l) for l in range(L)])
+                                    for t in range(n_in)]).view(np.int16)).to(dev)
+    if cfg.router:
+        wr = torch.from_numpy(np.stack([W.router_weights(cfg, l) for l in range(L)]).view(np.int16)).to(dev)
+        lo = torch.empty((L, B, Ex), dtype=torch.float32, device=dev)
+    else:
+        logits = torch.from_numpy(np.stack([np.stack([W.given_logits(cfg, t, l) for l in range(L)])
+                                            for t in range(n_in)]).view(np.int16)).to(dev)
+    y = torch.empty((L, B, d), dtype=torch.float32, device=dev)
+    dims = E.moe_dims(d, f, Ex, K)
+    pipe = StagedPipeline(dims, L, B, S, E.stack_from_bundles(store, d, f, bb, Ex * bb),
+                          E.stack_from_bundles(pool, d, f, bb, S * bb), device=dev, side_stream=not args.no_overlap)
+    rp = E.route_params(cfg.mode, K, cfg.n_groups, cfg.topk_groups, cfg.scale, cfg.eps)
+
+    def route(buf, t, on_side):
+        if cfg.router:
+            pipe.route_router(buf, rp, xs[t % n_in], wr, lo, on_side=on_side)
+        else:
+            pipe.route_given(buf, rp, logits[t % n_in], on_side=on_side)
+
+    ev_dec, ev_upd = events(args.steps), events(args.steps)
+    route(0, 0, False)
+    pipe.update(0, None)
+    pipe.join()
+
+    def step(t, rec):
+        nb, cb = (t + 1) % 2, t % 2
+        pipe.side_after_main()
+        if rec is not None:
+            ev_upd[rec][0].record(pipe.side)
+        route(nb, t + 1, True)
+        pipe.update(nb, cb, after_main=False)
+        if rec is not None:
+            ev_upd[rec][1].record(pipe.side)
+            ev_dec[rec][0].record(pipe.main)
+        pipe.decode(cb, xs[t % n_in], y)
+        if rec is not None:
+            ev_dec[rec][1].record(pipe.main)
+        pipe.join()
+
+    wall = run_steps(args, step)
+    if int(pipe.err.item()):
+        raise RuntimeError(f"device error bits {int(pipe.err.item())}")
+    # Distinct experts per layer per step (what the decode must read), from the
+    # routing of the input steps, outside the timed region.
+    uniq = []
+    for s in range(min(n_in, 16)):
+        route(0, s, False)
+        torch.cuda.synchronize()
+        ids = pipe.idx[0].cpu().numpy().reshape(L, -1)
+        uniq.append(np.mean([len(np.unique(r)) for r in ids]))
+    dec_ms, upd_ms = mean_ms(ev_dec), mean_ms(ev_upd)
+    algo_bytes = int(round(L * float(np.mean(uniq)) * bb))
+    achieved = algo_bytes / (dec_ms * 1e-3) / 1e9
+    return dict(value=round(args.steps * B / wall, 2), unit=f"tok/s ({L}-layer MoE stack, batch {B})",
+                ms_per_step=round(wall * 1e3 / args.steps, 5),
+                config={"workload": f"{cfg.name}: staged decode, {L} layers x {Ex} experts, d_model {d}, d_ff {f}, "
+                                    f"{'sigmoid-group' if cfg.mode else 'softmax'} top-{K}, batch {B}, "
+                                    f"{S} slots/layer",
+                        "layers": L, "experts": Ex, "d_model": d, "d_ff": f, "top_k": K, "batch": B, "slots": S},
+                layer_tok_per_s=round(args.steps * B * L / wall, 1),
+                decode_call_us=round(dec_ms * 1e3, 2), route_and_slot_update_us=round(upd_ms * 1e3, 2),
+                slot_copies_last_step=int(pipe.n_copied.sum().item()), overlap=not args.no_overlap,
+                roofline={"bound": "hbm", "kernel": "e0_moe_staged_decode (gate/up + down launches)",
+                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                          "algorithmic_bytes_per_launch": algo_bytes,
+                          "unit_of_work": f"{np.mean(uniq):.2f} distinct experts x {bb} B per layer, {L} layers"})
+
+
+def cpu_decode(cfg, n_steps):
+    """Oracle staged decode (routing, slot rule, expert FFNs) on a sample of steps."""
+    import oracle
+    from e0inputs import gen, workloads as W
+
+    threads = host_threads(cfg.L)
+    steps = n_steps or (1 if cfg.B > 1 else max(1, min(8, threads // 2)))
+    t_total = 0.0
+    for t in range(steps):
+        pools, slot_of, xs, idxs, ws = [], [], [], [], []
+        for l in range(cfg.L):
+            x = W.activations(cfg, t, l)
+            lg = (oracle.router_logits(x, W.router_weights(cfg, l)) if cfg.router
+                  else W.given_logits(cfg, t, l).astype(np.float32))
+            idx, w = oracle.route(lg, cfg)
+            so = np.full(cfg.E, -1, np.int32)
+            eo = np.full(cfg.S, -1, np.int32)
+            oracle.slot_update(cfg.E, cfg.S, idx, [], so, eo)
+            mats = {int(e): gen.expert(cfg.seed, l, int(e), cfg.d, cfg.f) for e in eo if e >= 0}
+            first = next(iter(mats.values()))
+            pools += [mats.get(int(e), first) for e in eo]
+            slot_of.append(so)
+            xs.append(x)
+            idxs.append(idx)
+            ws.append(w)
+        P = oracle.Experts(pools)
+        t0 = time.perf_counter()
+        oracle.decode_layers(P, cfg.S, np.stack(slot_of), cfg.E, cfg.d, cfg.f, np.stack(xs), np.stack(idxs),
+                             np.stack(ws), n_threads=threads)
+        t_total += time.perf_counter() - t0
+    return {"value": round(steps * cfg.B / t_total, 4), "unit": f"tok/s ({cfg.L}-layer MoE stack, batch {cfg.B})",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{steps} decode step(s) x {cfg.L} layers at batch {cfg.B}: staged FFNs of the fp64 C oracle, "
+                      f"{threads} threads over layers; {t_total:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
+# sorted prefill (35B tier, one layer)
+# ---------------------------------------------------------------------------
+
+def bench_prefill(args, cfg):
+    import torch
+
+    from e0inputs import gen, gpu as G, workloads as W
+    from int4_gather_swiglu_amd import _lib as E
+
+    dev = torch.device("cuda:0")
+    T, K, Ex, d, f = cfg.B, cfg.K, cfg.E, cfg.d, cfg.f
+    bb = gen.bundle_bytes(d, f)
+    store = torch.empty((Ex, bb), dtype=torch.uint8, device=dev)
+    G.fill_experts(store.data_ptr(), bb, cfg.seed, 0, range(Ex), d, f)
+    x = torch.from_numpy(W.activations(cfg, 0, 0).view(np.int16)).to(dev)
+    lg = torch.from_numpy(W.given_logits(cfg, 0, 0)[None].view(np.int16)).to(dev)
+    idx = torch.empty((1, T, K), dtype=torch.int32, device=dev)
+    w = torch.empty((1, T, K), dtype=torch.float32, device=dev)
+    y = torch.empty((T, d), dtype=torch.float32, device=dev)
+    err = torch.zeros((1,), dtype=torch.int32, device=dev)
+    dims = E.moe_dims(d, f, Ex, K)
+    ws = torch.empty(E.workspace_bytes(E.E0_OP_SORTED_PREFILL, dims, T), dtype=torch.uint8, device=dev)
+    layer = E.stack_from_bundles(store, d, f, bb, 0)
+    rp = E.route_params(0, K)
+    ev = events(args.steps)
+
+    def step(t, rec):
+        E.e0_route(rp, 1, T, Ex, lg, True, None, None, 0, idx, w, None)
+        if rec is not None:
+            ev[rec][0].record()
+        E.e0_moe_sorted_prefill(dims, T, x, idx, w, layer, y, ws, err)
+        if rec is not None:
+            ev[rec][1].record()
+
+    wall = run_steps(args, step)
+    if int(err.item()):
+        raise RuntimeError(f"device error bits {int(err.item())}")
+    ms = mean_ms(ev)
+    flops = 2.0 * T * K * 3 * d * f
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=Ex)
+    tfs = flops / (ms * 1e-3) / 1e12
+    return dict(value=round(args.steps * T / wall, 1), unit="tok/s (one MoE layer, T=2048 prefill)",
+                ms_per_step=round(wall * 1e3 / args.steps, 5),
+                config={"workload": f"{cfg.name}: sorted whole-layer prefill, T={T}, {Ex} experts, d_model {d}, "
+                                    f"d_ff {f}, softmax top-{K}, Zipf({cfg.zipf}) popularity",
+                        "tokens": T, "experts": Ex, "d_model": d, "d_ff": f, "top_k": K},
+                prefill_call_us=round(ms * 1e3, 2), active_experts=int((counts > 0).sum()),
+                top_expert_rows=int(counts.max()),
+                roofline={"bound": "mfma", "kernel": "e0_moe_sorted_prefill (sort + 2 grouped GEMMs + combine)",
+                          "achieved": round(tfs, 1), "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+                          "frac": round(tfs / MFMA_F16_PEAK_TFS, 4), "traffic": None,
+                          "algorithmic_flops_per_launch": flops,
+                          "unit_of_work": f"2*T*K*3*d*f = {flops:.4g} FLOP per layer forward"})
+
+
+def cpu_prefill(cfg, n_tok):
+    import oracle
+    from e0inputs import gen, workloads as W
+
+    tok = np.arange(n_tok or 16)
+    x = W.activations(cfg, 0, 0)[tok]
+    idx, w = oracle.softmax_topk(W.given_logits(cfg, 0, 0)[tok].astype(np.float32), cfg.K)
+    ids = sorted(set(idx.ravel().tolist()))
+    mats = {e: gen.expert(cfg.seed, 0, e, cfg.d, cfg.f) for e in ids}
+    lst = [mats.get(e, mats[ids[0]]) for e in range(cfg.E)]
+    t0 = time.perf_counter()
+    oracle.moe_sorted(oracle.Experts(lst), cfg.d, cfg.f, x, idx, w)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(tok) / dt, 4), "unit": "tok/s (one MoE layer)", "cores": 1, "kind": "oracle",
+            "sample": f"{len(tok)} of the {cfg.B} prefill tokens through the sorted ordering of the fp64 C oracle, "
+                      f"single thread; {dt:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
+# prerouted pipeline (35B tier, 32 staged layers)
+# ---------------------------------------------------------------------------
+
+def bench_prerouted(args, cfg, n_in):
+    import torch
+
+    from e0inputs import gen, gpu as G, workloads as W
+    from int4_gather_swiglu_amd import _lib as E
+    from int4_gather_swiglu_amd.pipeline import PrerouterPipeline
+
+    dev = torch.device("cuda:0")
+    L, K, Ex, S, d, f = cfg.L, cfg.K, cfg.E, cfg.S, cfg.d, cfg.f
+    bb = gen.bundle_bytes(d, f)
+
+    def f16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    store = torch.empty((L, Ex, bb), dtype=torch.uint8, device=dev)
+    for l in range(L):
+        G.fill_experts(store[l].data_ptr(), bb, cfg.seed, l, range(Ex), d, f)
+    pool = torch.zeros((L, S, bb), dtype=torch.uint8, device=dev)
+    heads = [W.head(cfg, j) for j in range(L)]
+    hd_t = [f16(np.stack([getattr(h, k) for h in heads])) for k in ("fc1_w", "fc1_b", "fc2_w", "fc2_b", "lin_w")]
+    bb_sh = gen.bundle_bytes(d, cfg.shared_f)
+    sh_store = torch.zeros((L, bb_sh), dtype=torch.uint8, device=dev)
+    for l in range(L):
+        G.fill_experts(sh_store[l].data_ptr(), bb_sh, cfg.seed, l, [0], d, cfg.shared_f, tag=gen.TAG_SHARED)
+    lor = [W.lora(cfg, l) for l in range(L)]
+    la = [f16(np.stack([lor[l][p][0] for l in range(L)])) for p in range(3)]
+    lb = [f16(np.stack([lor[l][p][1] for l in range(L)])) for p in range(3)]
+    P = W.prerouted_inputs(cfg, n_in)
+    hin = f16(P.hin[:, :, None, :])
+    owner0 = torch.from_numpy(P.owner0).to(dev)
+    dims = E.moe_dims(d, f, Ex, K)
+    shared = E.shared_from_tensors(sh_store, d, cfg.shared_f, la, lb, cfg.lora_alpha_over_r)
+    pipe = PrerouterPipeline(dims, L, 1, S, E.stack_from_bundles(store, d, f, bb, Ex * bb),
+                             E.stack_from_bundles(pool, d, f, bb, S * bb), E.heads_from_tensors(*hd_t),
+                             E.route_params(0, K), shared=shared, device=dev, side_stream=not args.no_overlap)
+    R = torch.zeros((3, L + 1, 1, K), dtype=torch.int32, device=dev)
+    Wt = torch.full((3, L + 1, 1, K), 1.0 / K, dtype=torch.float32, device=dev)
+    R[0, 0, 0] = owner0[0]
+    R[0, 1:, 0] = torch.from_numpy(P.r0).to(dev)
+    y = torch.empty((L, 1, d), dtype=torch.float32, device=dev)
+    ev_dec, ev_pre = events(args.steps), events(args.steps)
+    pipe.update_ids(R[0, 1:], None)
+    pipe.join()
+
+    def step(t, rec):
+        c, n, p = t % 3, (t + 1) % 3, (t - 1) % 3
+        R[n, 0, 0].copy_(owner0[(t + 1) % n_in])
+        if rec is not None:
+            ev_pre[rec][0].record()
+        pipe.predict(hin[t % n_in], R[c], R[p] if t > 0 else None, R[n], Wt[n])
+        if rec is not None:
+            ev_pre[rec][1].record()
+        pipe.update_ids(R[n, 1:], R[c, 1:])
+        if rec is not None:
+            ev_dec[rec][0].record()
+        pipe.decode_ids(R[c, 1:], Wt[c, 1:], hin[t % n_in, 1:], y)
+        if rec is not None:
+            ev_dec[rec][1].record()
+        pipe.join()
+
+    wall = run_steps(args, step)
+    if int(pipe.err.item()):
+        raise RuntimeError(f"device error bits {int(pipe.err.item())}")
+    dec_ms, pre_ms = mean_ms(ev_dec), mean_ms(ev_pre)
+    r = cfg.lora_r
+    lora_bytes = L * 2 * (r * d + cfg.shared_f * r + r * d + cfg.shared_f * r + r * cfg.shared_f + d * r)
+    algo_bytes = L * K * bb + L * bb_sh + lora_bytes
+    achieved = algo_bytes / (dec_ms * 1e-3) / 1e9
+    head_bytes = L * W.head_weight_bytes(cfg)
+    return dict(value=round(args.steps / wall, 2), unit=f"tok/s ({L} staged layers + heads, batch 1)",
+                ms_per_step=round(wall * 1e3 / args.steps, 5),
+                config={"workload": f"{cfg.name}: heads -> slot update || staged decode + shared expert + LoRA r{r},"
+                                    f" {L} layers x {Ex} experts, d_model {d}, d_ff {f}, top-{K}, "
+                                    f"repeat p={cfg.repeat_p}",
+                        "layers": L, "experts": Ex, "d_model": d, "d_ff": f, "top_k": K, "batch": 1, "slots": S},
+                decode_call_us=round(dec_ms * 1e3, 2), prerouter_call_us=round(pre_ms * 1e3, 2),
+                prerouter_GBps=round(head_bytes / (pre_ms * 1e-3) / 1e9, 1),
+                slot_copies_last_step=int(pipe.n_copied.sum().item()), overlap=not args.no_overlap,
+                roofline={"bound": "hbm", "kernel": "e0_moe_staged_decode (routed + shared + LoRA)",
+                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                          "algorithmic_bytes_per_launch": int(algo_bytes),
+                          "unit_of_work": f"{K} routed experts x {bb} B + shared {bb_sh} B + LoRA per layer, "
+                                          f"{L} layers"})
 
 
 def main():
@@ -47,146 +377,35 @@ def main():
         sys.exit(2)
     import torch
 
-    from e0inputs import gen, gpu as G, workloads as W
-    from int4_gather_swiglu_amd import _lib as E
-    from int4_gather_swiglu_amd.pipeline import StagedPipeline
-
-    cfg = W.DECODE35
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    L, B, K, Ex, S, d, f = cfg.L, cfg.B, cfg.K, cfg.E, cfg.S, cfg.d, cfg.f
-    bb = gen.bundle_bytes(d, f)
-    n_in = cfg.steps  # distinct input steps (256), reused cyclically
-
-    # Inputs: the full expert store (18.1 GB) filled on the GPU; per-step fp16
-    # logits and activations drawn on the host and made resident in HBM.
-    store = torch.empty((L, Ex, bb), dtype=torch.uint8, device=dev)
-    for l in range(L):
-        G.fill_experts(store[l].data_ptr(), bb, cfg.seed, l, range(Ex), d, f)
-    pool = torch.zeros((L, S, bb), dtype=torch.uint8, device=dev)
-    logits = torch.from_numpy(np.stack([np.stack([W.given_logits(cfg, t, l) for l in range(L)])
-                                        for t in range(n_in)]).view(np.int16)).to(dev)
-    xs = torch.from_numpy(np.stack([np.stack([W.activations(cfg, t, l) for l in range(L)])
-                                    for t in range(n_in)]).view(np.int16)).to(dev)
-    y = torch.empty((L, B, d), dtype=torch.float32, device=dev)
-    dims = E.moe_dims(d, f, Ex, K)
-    st_store = E.stack_from_bundles(store, d, f, bb, Ex * bb)
-    st_pool = E.stack_from_bundles(pool, d, f, bb, S * bb)
-    pipe = StagedPipeline(dims, L, B, S, st_store, st_pool, device=dev, side_stream=not args.no_overlap)
-    rp = E.route_params(0, K)
-
-    ev_dec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    ev_upd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-
-    pipe.route_given(0, rp, logits[0])
-    pipe.update(0, None)
-    pipe.join()
-
-    def step(t, rec=None):
-        nb, cb = (t + 1) % 2, t % 2
-        pipe.side_after_main()
-        if rec is not None:
-            ev_upd[rec][0].record(pipe.side)
-        pipe.route_given(nb, rp, logits[(t + 1) % n_in], on_side=True)
-        pipe.update(nb, cb, after_main=False)
-        if rec is not None:
-            ev_upd[rec][1].record(pipe.side)
-            ev_dec[rec][0].record(pipe.main)
-        pipe.decode(cb, xs[t % n_in], y)
-        if rec is not None:
-            ev_dec[rec][1].record(pipe.main)
-        pipe.join()
-
-    t = 0
-    for _ in range(args.warmup):
-        step(t)
-        t += 1
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(t, i)
-        t += 1
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    err = int(pipe.err.item())
-    if err:
-        print(f"bench.py: device error bits {err}", file=sys.stderr)
-        sys.exit(3)
-
-    ms_step = wall * 1e3 / args.steps
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_dec]))
-    upd_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_upd]))
-    algo_bytes = L * B * K * bb  # one expert bundle per (layer, k) at batch 1 (distinct ids per token)
-    achieved = algo_bytes / (dec_ms * 1e-3) / 1e9
-    copies = int(pipe.n_copied.sum().item())
-
-    out = {
-        "metric": "MoE-layer tok/s + achieved HBM GB/s (decode) / MFMA util (prefill), int4 g64",
-        "value": round(args.steps * B / wall, 2),
-        "unit": "tok/s (40-layer MoE stack, batch 1)",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "int4 g64 weights, fp16 activations, fp32 accumulate",
-        "data": "synthetic (seeded; int4 codes U{0..15}, fp16 scale U(0.005,0.02), bias -8s(1+U(-0.1,0.1)))",
-        "config": {"workload": "decode35b: staged decode, 40 layers x 256 experts, d_model 2048, d_ff 512, "
-                               "top-4 softmax, batch 1, 2x4 slots/layer",
-                   "layers": L, "experts": Ex, "d_model": d, "d_ff": f, "top_k": K, "batch": B, "slots": S},
-        "layer_tok_per_s": round(args.steps * B * L / wall, 1),
-        "decode_call_us": round(dec_ms * 1e3, 2),
-        "route_and_slot_update_us": round(upd_ms * 1e3, 2),
-        "slot_copies_last_step": copies,
-        "overlap": not args.no_overlap,
-        "roofline": {"bound": "hbm", "kernel": "e0_moe_staged_decode (gate/up + down launches)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "algorithmic_bytes_per_launch": algo_bytes},
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_steps)
+    from e0inputs import workloads as W
+    torch.cuda.set_device(0)
+    wl = args.workload
+    cpu = None
+    if wl == "decode35b":
+        res = bench_decode(args, W.DECODE35, W.DECODE35.steps)
+        cpu = (lambda: cpu_decode(W.DECODE35, args.cpu_steps))
+    elif wl == "prefill35b":
+        res = bench_prefill(args, W.PREFILL35)
+        cpu = (lambda: cpu_prefill(W.PREFILL35, args.cpu_steps))
+    elif wl == "decode8b_b1":
+        res = bench_decode(args, W.DECODE8_B1, 64)
+        cpu = (lambda: cpu_decode(W.DECODE8_B1, args.cpu_steps))
+    elif wl == "decode8b_b32":
+        res = bench_decode(args, W.DECODE8_B32, 8)
+        cpu = (lambda: cpu_decode(W.DECODE8_B32, args.cpu_steps))
+    else:
+        res = bench_prerouted(args, W.PREROUTED35, 32)
+    out = {"metric": METRIC, "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None,
+           "dtype": ("int4 g64 weights dequantised to fp16, fp16 MFMA, fp32 accumulate" if wl == "prefill35b"
+                     else "int4 g64 weights, fp16 activations, fp32 accumulate"),
+           "data": "synthetic (seeded; int4 codes U{0..15}, fp16 scale U(0.005,0.02), bias -8s(1+U(-0.1,0.1)))",
+           "config": res.pop("config")}
+    out.update(res)
+    if not args.no_cpu_baseline and cpu is not None:
+        out["cpu_baseline"] = cpu()
     print(json.dumps(out), flush=True)
-
-
-def cpu_baseline(cfg, n_steps):
-    """The CPU oracle on a bounded sample of the same workload: the staged
-    decode of `n_steps` steps x 40 layers at batch 1, threads = host cores."""
-    import oracle
-    from e0inputs import gen, workloads as W
-
-    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    threads = max(1, min(threads, cfg.L))
-    steps = n_steps or max(1, min(8, threads // 2))
-    t_total = 0.0
-    for t in range(steps):
-        pools, slot_of, xs, idxs, ws = [], [], [], [], []
-        for l in range(cfg.L):
-            lg = W.given_logits(cfg, t, l).astype(np.float32)
-            idx, w = oracle.softmax_topk(lg, cfg.K)
-            so = np.full(cfg.E, -1, np.int32)
-            eo = np.full(cfg.S, -1, np.int32)
-            oracle.slot_update(cfg.E, cfg.S, idx, [], so, eo)
-            mats = {int(e): gen.expert(cfg.seed, l, int(e), cfg.d, cfg.f) for e in eo if e >= 0}
-            first = next(iter(mats.values()))
-            pools += [mats.get(int(e), first) for e in eo]
-            slot_of.append(so)
-            xs.append(W.activations(cfg, t, l))
-            idxs.append(idx)
-            ws.append(w)
-        P = oracle.Experts(pools)
-        t0 = time.perf_counter()
-        oracle.decode_layers(P, cfg.S, np.stack(slot_of), cfg.E, cfg.d, cfg.f, np.stack(xs), np.stack(idxs),
-                             np.stack(ws), n_threads=threads)
-        t_total += time.perf_counter() - t0
-    return {"value": round(steps * cfg.B / t_total, 4), "unit": "tok/s (40-layer MoE stack, batch 1)",
-            "cores": threads, "kind": "oracle",
-            "sample": f"{steps} decode steps x {cfg.L} layers (staged decode only, fp64 C oracle, "
-                      f"{threads} threads over layers); {t_total:.1f} s"}
 
 
 if __name__ == "__main__":

@@ -217,15 +217,16 @@ e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, int32_t B, co
 /*
  * e0_moe_sorted_prefill — the whole-layer path (jaehun.me report 3.1;
  * discuss.pytorch.kr paths table: a layer's experts all resident, then a
- * sorted gather): the T*K (token, k) pairs are sorted stably by expert, each
- * active expert runs as one grouped GEMM over its rows (matrix cores), and the
- * weighted results are summed back in token order:
+ * sorted gather): the T*K (token, k) pairs are grouped by expert (the order
+ * of the rows inside an expert's group is unspecified; no result depends on
+ * it), each active expert runs as one grouped GEMM over its rows (matrix
+ * cores), and the weighted results are summed back per token in k order:
  *   y[t] = sum_k w[t][k] * down(silu(gate(x_t)) * up(x_t)) of expert idx[t][k].
  *  x: device fp16 [T][d]; idx, w: device [T][K]; layer: slot e = expert e
  *  (layer_stride unused); y: device fp32 [T][d] (overwritten).
  *  ws: device workspace, e0_workspace_bytes(E0_OP_SORTED_PREFILL, dims, T, 0, 0).
  *  dev_err: device int32, OR-ed with E0_DEV_BAD_ID.
- *  Limits: d_model, d_ff multiples of 64; E <= 1024.
+ *  Limits: d_model, d_ff multiples of 128; E <= 1024; K <= 32; T*K <= 2^24.
  */
 e0_status e0_moe_sorted_prefill(const e0_moe_dims *dims, int32_t T, const uint16_t *x, const int32_t *idx,
                                 const float *w, const e0_stack *layer, float *y, void *ws, size_t ws_bytes,

@@ -16,11 +16,12 @@
 //    report 3.3), LoRA on the shared-expert projections only (koala.ai.kr
 //    training phase 2).
 //
-// Kernels (one call = up to three launches on the caller's stream):
-//  1. prep   (grid L): per layer, a stable counting sort of the (token, k)
-//     pairs by expert (the deduplicated expert set and each expert's tokens),
-//     and the LoRA down-projections A x of the shared expert. Skipped when
-//     B == 1 and there is no LoRA.
+// Kernels (one call = up to four launches on the caller's stream):
+//  1. prep   (grid L, B > 1 only): per layer, a stable counting sort of the
+//     (token, k) pairs by expert (the deduplicated expert set and each
+//     expert's tokens).
+//     lora   (shared expert with LoRA only): the down-projections A x, one
+//     wavefront per dot product.
 //  2. gateup (grid L x experts x row-chunks): each workgroup streams a block
 //     of gate and up rows of one expert once and applies them to all of its
 //     tokens: h = silu(gate x) * up x, written as fp32.
@@ -109,7 +110,7 @@ E0_DEV int block_exclusive_scan(int v, int *lds4, int &total) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. prep: dedup plan + LoRA A x for the shared expert.
+// 1. prep: dedup plan (B > 1); LoRA A x for the shared expert (own kernel).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void decode_prep_kernel(DecodeArgs a) {
     __shared__ int s_cnt[kMaxE];
@@ -179,27 +180,29 @@ __global__ __launch_bounds__(kThreads) void decode_prep_kernel(DecodeArgs a) {
         }
     }
 
-    if (a.has_shared && a.r > 0) {
-        // lora_a[l][t][p][i] = A_p[i] . x_t for gate and up (p = 0, 1).
-        const int lane = tid & 63, wv = tid >> 6;
-        const int jobs = a.B * 2 * a.r;
-        for (int job = wv; job < jobs; job += kWaves) {
-            const int t = job / (2 * a.r), rem = job % (2 * a.r), p = rem / a.r, i = rem % a.r;
-            const uint16_t *arow = a.la[p] + (int64_t)l * (a.la_ls[p] / 2) + (int64_t)i * a.d;
-            const uint16_t *xt = a.x + ((int64_t)l * a.B + t) * a.d;
-            float acc = 0.0f;
-            for (int c = lane * 8; c < a.d; c += 512) {
-                u32x4 av = *reinterpret_cast<const u32x4 *>(arow + c);
-                u32x4 xv = *reinterpret_cast<const u32x4 *>(xt + c);
+}
+
+// LoRA down-projections of the shared expert's inputs:
+// lora_a[l][t][p][i] = A_p[i] . x_t for gate and up (p = 0, 1); one wavefront
+// per dot product, spread over the whole grid.
+__global__ __launch_bounds__(kThreads) void decode_lora_kernel(DecodeArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int job = blockIdx.x * kWaves + wave_id();
+    const int per_layer = a.B * 2 * a.r;
+    if (job >= a.L * per_layer) return;
+    const int l = job / per_layer, rem = job % per_layer;
+    const int t = rem / (2 * a.r), p = (rem / a.r) % 2, i = rem % a.r;
+    const uint16_t *arow = a.la[p] + (int64_t)l * (a.la_ls[p] / 2) + (int64_t)i * a.d;
+    const uint16_t *xt = a.x + ((int64_t)l * a.B + t) * a.d;
+    float acc = 0.0f;
+    for (int c = lane * 8; c < a.d; c += 512) {
+        const u32x4 av = *reinterpret_cast<const u32x4 *>(arow + c);
+        const u32x4 xv = *reinterpret_cast<const u32x4 *>(xt + c);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc = __builtin_amdgcn_fdot2(as_h2(av[j]), as_h2(xv[j]),
-                                                 acc, false);
-            }
-            acc = wave_sum(acc);
-            if (lane == 0) a.lora_a[(((int64_t)l * a.B + t) * 3 + p) * a.r + i] = acc;
-        }
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_fdot2(as_h2(av[j]), as_h2(xv[j]), acc, false);
     }
+    acc = wave_sum(acc);
+    if (lane == 0) a.lora_a[(((int64_t)l * a.B + t) * 3 + p) * a.r + i] = acc;
 }
 
 // Group reduce-scatter over aligned groups of G lanes (G a power of two).
@@ -1021,8 +1024,13 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     e0_status s;
-    if (a.has_plan || (a.has_shared && r > 0)) {
+    if (a.has_plan) {
         hipLaunchKernelGGL(decode_prep_kernel, dim3(L), dim3(kThreads), 0, st, a);
+        if ((s = e0_launch_status())) return s;
+    }
+    if (a.has_shared && r > 0) {
+        const int64_t jobs = (int64_t)L * B * 2 * r;
+        hipLaunchKernelGGL(decode_lora_kernel, dim3((unsigned)((jobs + kWaves - 1) / kWaves)), dim3(kThreads), 0, st, a);
         if ((s = e0_launch_status())) return s;
     }
     if (B == 1 && lpr_d == 64) {

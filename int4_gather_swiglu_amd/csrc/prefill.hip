@@ -10,10 +10,9 @@
 // y_t = sum_k w_tk FFN_{e_tk}(x_t).
 //
 // Launches (one stream):
-//  1. sort     (1 workgroup): stable counting sort of the T*K pairs by expert
-//               (per-segment histograms, one scan, sequential per-segment
-//               scatter), the row offset of every expert and the list of
-//               128-row M-tiles.
+//  1. sort     (1 workgroup): counting sort of the T*K pairs by expert (LDS
+//               counters, one scan, scatter), the row offset of every
+//               expert and the list of 128-row M-tiles.
 //  2. gemm1    (tiles x d_ff/128): H = silu(X G^T) * (X U^T) for one M-tile
 //               and 128 columns of d_ff, X gathered through the sort; H fp16.
 //  3. gemm2    (tiles x d_model/128): Yb[pair] = w_pair * (H D^T).
@@ -37,7 +36,7 @@ constexpr int kTM = 128;         // rows per M-tile
 constexpr int kTN = 128;         // columns per workgroup (4 waves x 32)
 constexpr int kGemmThreads = 256;
 constexpr int kSortThreads = 1024;
-constexpr int kSortHistBytes = 32768;  // LDS for the per-segment histograms (uint16)
+constexpr int kMaxSortE = 1024;
 constexpr int kARowPad = 72;     // halves per LDS row of A (64 + 8 padding)
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -59,7 +58,6 @@ struct PrefillArgs {
     uint16_t *H;        // [n][f] fp16
     float *Yb;          // [n][d] weighted down outputs, by pair index
     int max_tiles;
-    int segs;           // histogram segments
 };
 
 // ---------------------------------------------------------------------------
@@ -87,60 +85,53 @@ E0_DEV int block_scan_1024(int v, int *lds16, int &total) {
 }
 
 __global__ __launch_bounds__(kSortThreads) void prefill_sort_kernel(PrefillArgs a) {
-    __shared__ uint16_t s_hist[kSortHistBytes / 2];  // [E][segs], expert-major
+    __shared__ int s_cnt[kMaxSortE];
+    __shared__ int s_fill[kMaxSortE];
     __shared__ int s_scan[kSortThreads / 64];
     const int tid = threadIdx.x;
-    const int S = a.segs, E = a.E, n = a.n;
-    const int seg_len = (n + S - 1) / S;
-    for (int i = tid; i < E * S; i += kSortThreads) s_hist[i] = 0;
+    const int E = a.E, n = a.n;
+    for (int e = tid; e < E; e += kSortThreads) s_cnt[e] = s_fill[e] = 0;
     __syncthreads();
-    // Per-segment histograms: thread s counts its segment (no atomics needed).
-    if (tid < S) {
-        for (int p = tid * seg_len; p < n && p < (tid + 1) * seg_len; ++p) {
-            const int e = a.idx[p];
-            if (e >= 0 && e < E)
-                s_hist[e * S + tid]++;
-            else
-                set_err(a.err, E0_DEV_BAD_ID);
-        }
+    // Counts per expert (LDS atomics; the counts do not depend on their order).
+    for (int p = tid; p < n; p += kSortThreads) {
+        const int e = a.idx[p];
+        if (e >= 0 && e < E)
+            atomicAdd(&s_cnt[e], 1);
+        else
+            set_err(a.err, E0_DEV_BAD_ID);
     }
     __syncthreads();
-    // Exclusive scan over (expert, segment) in expert-major order.
-    const int per = (E * S + kSortThreads - 1) / kSortThreads;
-    int local = 0;
-    for (int i = tid * per; i < (tid + 1) * per && i < E * S; ++i) local += s_hist[i];
-    int total;
-    int run = block_scan_1024(local, s_scan, total);
-    for (int i = tid * per; i < (tid + 1) * per && i < E * S; ++i) {
-        const int c = s_hist[i];
-        s_hist[i] = (uint16_t)run;  // now the base of (expert, segment); n < 65536
-        if (i % S == 0) a.off[i / S] = run;
-        run += c;
-    }
-    if (tid == 0) a.off[E] = total;
-    __syncthreads();
-    // Stable scatter: each segment walks its pairs in order.
-    if (tid < S) {
-        for (int p = tid * seg_len; p < n && p < (tid + 1) * seg_len; ++p) {
-            const int e = a.idx[p];
-            if (e >= 0 && e < E) a.perm[s_hist[e * S + tid]++] = p;
-        }
-    }
-    __syncthreads();
-    // M-tiles: ceil(count / kTM) per expert, in expert order.
+    // Exclusive scan -> first sorted row of each expert; tiles per expert.
     const int eper = (E + kSortThreads - 1) / kSortThreads;
-    int nt = 0;
-    for (int e = tid * eper; e < (tid + 1) * eper && e < E; ++e) nt += (a.off[e + 1] - a.off[e] + kTM - 1) / kTM;
-    int tt;
+    int local = 0, nt = 0;
+    for (int e = tid * eper; e < (tid + 1) * eper && e < E; ++e) {
+        local += s_cnt[e];
+        nt += (s_cnt[e] + kTM - 1) / kTM;
+    }
+    int total, tt;
+    int run = block_scan_1024(local, s_scan, total);
     int tb = block_scan_1024(nt, s_scan, tt);
     for (int e = tid * eper; e < (tid + 1) * eper && e < E; ++e) {
-        const int o = a.off[e], c = a.off[e + 1] - o;
-        for (int m = 0; m < c; m += kTM, ++tb) {
+        a.off[e] = run;
+        s_fill[e] = run;
+        for (int m = 0; m < s_cnt[e]; m += kTM, ++tb) {
             a.tile_e[tb] = e;
-            a.tile_m0[tb] = o + m;
+            a.tile_m0[tb] = run + m;
         }
+        run += s_cnt[e];
     }
-    if (tid == 0) a.ntiles[0] = tt;
+    if (tid == 0) {
+        a.off[E] = total;
+        a.ntiles[0] = tt;
+    }
+    __syncthreads();
+    // Scatter. The order of rows inside an expert's block follows the LDS
+    // atomics and may differ from run to run; no output depends on it (every
+    // GEMM row is computed on its own and results are stored by pair index).
+    for (int p = tid; p < n; p += kSortThreads) {
+        const int e = a.idx[p];
+        if (e >= 0 && e < E) a.perm[atomicAdd(&s_fill[e], 1)] = p;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -373,7 +364,7 @@ extern "C" e0_status e0_moe_sorted_prefill(const e0_moe_dims *dims, int32_t T, c
     E0_REQUIRE(d > 0 && f > 0 && d % kTN == 0 && f % kTN == 0, E0_ERR_UNSUPPORTED_SHAPE);
     E0_REQUIRE(K <= E && E <= 1024 && K <= 32, E0_ERR_UNSUPPORTED_SHAPE);
     const int64_t n = (int64_t)T * K;
-    E0_REQUIRE(n < 65536, E0_ERR_CAPACITY);
+    E0_REQUIRE(n <= (1 << 24), E0_ERR_CAPACITY);
     E0_REQUIRE(x && idx && w && y && dev_err, E0_ERR_INVALID_ARG);
     E0_REQUIRE(stack_ok(layer), E0_ERR_INVALID_ARG);
     E0_REQUIRE((reinterpret_cast<uintptr_t>(x) & 15) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0,
@@ -406,10 +397,6 @@ extern "C" e0_status e0_moe_sorted_prefill(const e0_moe_dims *dims, int32_t T, c
     a.H = reinterpret_cast<uint16_t *>(wsb + lay.H);
     a.Yb = reinterpret_cast<float *>(wsb + lay.Yb);
     a.max_tiles = lay.max_tiles;
-    int segs = (kSortHistBytes / 2) / E;
-    if (segs > kSortThreads) segs = kSortThreads;
-    if (segs > (int)n) segs = (int)n;
-    a.segs = segs < 1 ? 1 : segs;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     e0_status s;
