@@ -58,7 +58,8 @@ enum {
 enum {
     E0_DEV_BAD_ID = 1,       /* routed id < 0 or >= E */
     E0_DEV_NOT_RESIDENT = 2, /* routed id has no slot in the slot table */
-    E0_DEV_NO_SLOT = 4       /* slot update found no free slot for a missing expert */
+    E0_DEV_NO_SLOT = 4,      /* slot update found no free slot for a missing expert */
+    E0_DEV_SYNC_TIMEOUT = 8  /* an in-launch wait between workgroups expired (outputs invalid) */
 };
 
 /* Routing math (jaehun.me review, report Appx. A; the same math routes both

@@ -2,12 +2,26 @@
 // workspace sizes of the five calls.
 #include "e0_internal.h"
 
+#include <atomic>
+
 size_t e0_decode_workspace_bytes(const e0_moe_dims *dims, int32_t L, int32_t B, int32_t r);
 size_t e0_slot_workspace_bytes(const e0_moe_dims *dims, int32_t L, int32_t B, int32_t S);
 size_t e0_prerouter_workspace_bytes(int32_t H, int32_t B, int32_t E, int32_t hid);
 size_t e0_prefill_workspace_bytes(const e0_moe_dims *dims, int32_t T);
 
 extern "C" int32_t e0_abi_version(void) { return E0_ABI_VERSION; }
+
+// Epochs of the in-launch hand-off flags: a process-wide call counter passed
+// through a 64-bit bijective mixer (Stafford's "Mix13" finaliser), so that a
+// flag word left over from other data is unlikely to equal the epoch.
+uint64_t e0_next_epoch() {
+    static std::atomic<uint64_t> calls{0};
+    uint64_t z = calls.fetch_add(1, std::memory_order_relaxed) + 1;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return z ? z : 1;
+}
 
 extern "C" const char *e0_status_string(e0_status s) {
     switch (s) {

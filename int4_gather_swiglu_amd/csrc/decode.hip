@@ -74,6 +74,14 @@ struct DecodeArgs {
     int32_t *pairs;  // [L][B*K]
     float *hbuf;     // [L][B*K + B][f]
     float *lora_a;   // [L][B][3][r]
+    uint32_t *hblk;  // [L][units][d_ff / 32][kBlk] (single-launch batch-1 path)
+    // single-launch batch-1 path
+    uint64_t *flags;  // [L] lora items, then [L][units][nch] gate/up items
+    uint64_t epoch;
+    int units;        // K + (shared expert ? 1 : 0)
+    int nch;          // gate/up items per unit (d_ff / kFuseCh)
+    int n_lora;       // lora items (L with LoRA, else 0)
+    int n_gu;         // gate/up items (L * units * nch)
 };
 
 E0_DEV int pairs_per_layer(const DecodeArgs &a) { return a.B * a.K + a.B; }
@@ -276,6 +284,71 @@ E0_DEV float dot_word(uint32_t w, const uint32_t (&xp)[4], float acc, NibbleCons
     return acc;
 }
 E0_DEV float dot_word(uint32_t w, const uint32_t (&xp)[4], float acc) { return dot_word(w, xp, acc, nibble_consts()); }
+
+// Nibble placement with a 1024 offset, no shifts for half of the codes:
+// (w & m) | 0x64006400 gives, per fp16 half, 1024 + q for a nibble at bits
+// 0..3 of the half and 1024 + 16 q for a nibble at bits 4..7 (exact).
+struct MagicConsts {
+    uint32_t lo, hi, one;
+};
+E0_DEV MagicConsts magic_consts() {
+    MagicConsts k;
+    __asm__("v_mov_b32 %0, 0x000f000f" : "=v"(k.lo));
+    __asm__("v_mov_b32 %0, 0x00f000f0" : "=v"(k.hi));
+    __asm__("v_mov_b32 %0, 0x64006400" : "=v"(k.one));
+    return k;
+}
+
+// Over the 8 codes of `w`: sum of (1024 + q_c) v_c for c in {0, 2, 4, 6} and
+// (1024 + 16 q_c) (v_c / 16) for c in {1, 3, 5, 7}, with v given as the pairs
+// (v0, v4), (v1/16, v5/16), (v2, v6), (v3/16, v7/16). The result is
+// sum(q v) + 1024 (v0 + v2 + v4 + v6) + 64 (v1 + v3 + v5 + v7).
+E0_DEV float dot_word_m(uint32_t w, const uint32_t *vp, float acc, MagicConsts k) {
+    const uint32_t w8 = w >> 8;
+    acc = __builtin_amdgcn_fdot2(as_h2(and_or(w, k.lo, k.one)), as_h2(vp[0]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(and_or(w, k.hi, k.one)), as_h2(vp[1]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(and_or(w8, k.lo, k.one)), as_h2(vp[2]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(and_or(w8, k.hi, k.one)), as_h2(vp[3]), acc, false);
+    return acc;
+}
+
+// The same with v split in two fp16 parts, vh + vl (hi = fp16(v), lo =
+// fp16(v - hi)), for fp32 inputs.
+E0_DEV float dot_word_m2(uint32_t w, const uint32_t *vh, const uint32_t *vl, float acc, MagicConsts k) {
+    const uint32_t w8 = w >> 8;
+    const uint32_t t0 = and_or(w, k.lo, k.one), t1 = and_or(w, k.hi, k.one);
+    const uint32_t t2 = and_or(w8, k.lo, k.one), t3 = and_or(w8, k.hi, k.one);
+    acc = __builtin_amdgcn_fdot2(as_h2(t0), as_h2(vh[0]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(t0), as_h2(vl[0]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(t1), as_h2(vh[1]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(t1), as_h2(vl[1]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(t2), as_h2(vh[2]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(t2), as_h2(vl[2]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(t3), as_h2(vh[3]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(t3), as_h2(vl[3]), acc, false);
+    return acc;
+}
+
+// Magic-offset pairs of 8 consecutive fp16 inputs (4 dwords), and their
+// plain sum and offset sum 1024 (v0 + v2 + v4 + v6) + 64 (v1 + v3 + v5 + v7).
+E0_DEV void x_pairs_m(const u32x4 v, uint32_t (&o)[4], float &sum, float &corr) {
+    x_pairs(v, o);
+    const f16x2 k16 = {(f16)0.0625f, (f16)0.0625f};
+    float se = 0.0f, so = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f16x2 hv = as_h2(o[j]);
+        const float t = (float)hv[0] + (float)hv[1];
+        if (j & 1) {
+            so += t;
+            o[j] = __builtin_bit_cast(uint32_t, hv * k16);
+        } else {
+            se += t;
+        }
+    }
+    sum += se + so;
+    corr += 1024.0f * se + 64.0f * so;
+}
 
 // ---------------------------------------------------------------------------
 // 2. gateup. Template: LPR lanes per row pass (d = 32 * LPR * NP), TC tokens
@@ -850,6 +923,336 @@ __global__ __launch_bounds__(kThreads) void decode_down_flat_kernel(DecodeArgs a
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Batch-1 single-launch decode. The work of a call is one list of items, one
+// workgroup each, in blockIdx order:
+//   lora items     (l)        A_gate x and A_up x of the shared expert's LoRA
+//   gate/up items  (l, u, c)  gate and up rows c*kFuseCh .. +kFuseCh of unit u
+//                             (routed expert k = u < K, shared expert u = K):
+//                             h[l][u][rows] = silu(gate x) * up x
+//   down items     (l, rb)    a block of output rows of layer l:
+//                             y = sum over units in k order of w_u down_u h_u
+// Consumers (down items; shared gate/up items with LoRA) wait for the flags
+// of their producers, which precede them in blockIdx order; a down item
+// issues its weight loads before it waits. One launch streams every weight
+// byte once with no gap between the gate/up and the down phases.
+// ---------------------------------------------------------------------------
+constexpr int kFuseCh = 32;      // hidden units per gate/up item (4 per wavefront)
+constexpr int kFuseThreads = 256;
+constexpr int kFuseWaves = kFuseThreads / kWave;
+constexpr int kBlk = 36;         // dwords per h block: 16 hi pairs, 16 lo pairs, sum, offset sum, 2 pad
+constexpr int kBlkSum = 32, kBlkCorr = 33;
+
+E0_DEV uint64_t *gu_flags(const DecodeArgs &a, int l) { return a.flags + a.L + (int64_t)l * a.units * a.nch; }
+
+// h block of (layer l, unit u, 32-column group g): the down input h[32g ..
+// 32g + 32) in the form the down dot product takes (see dot_word_m2).
+E0_DEV uint32_t *hblk(const DecodeArgs &a, int l, int u, int g) {
+    return a.hblk + (((int64_t)l * a.units + u) * (a.f / 32) + g) * kBlk;
+}
+
+E0_DEV void fused_lora_item(const DecodeArgs &a, int l) {
+    const int lane = threadIdx.x & 63, wv = wave_id();
+    const uint16_t *xt = a.x + (int64_t)l * a.d;
+    for (int job = wv; job < 2 * a.r; job += kFuseWaves) {
+        const int p = job / a.r, i = job % a.r;
+        const uint16_t *arow = a.la[p] + (int64_t)l * (a.la_ls[p] / 2) + (int64_t)i * a.d;
+        float acc = 0.0f;
+        for (int c = lane * 8; c < a.d; c += 512) {
+            const u32x4 av = *reinterpret_cast<const u32x4 *>(arow + c);
+            const u32x4 xv = *reinterpret_cast<const u32x4 *>(xt + c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_fdot2(as_h2(av[j]), as_h2(xv[j]), acc, false);
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) coherent_store(a.lora_a + ((int64_t)l * 3 + p) * a.r + i, acc);
+    }
+    signal_ready(a.flags + l, a.epoch);
+}
+
+// Slot of routed expert k of layer l (batch 1), or -1 (flagging the error
+// when `flag`).
+E0_DEV int routed_slot(const DecodeArgs &a, int l, int k, bool flag) {
+    const int e = a.idx[(int64_t)l * a.K + k];
+    if (e < 0 || e >= a.E) {
+        if (flag) set_err(a.err, E0_DEV_BAD_ID);
+        return -1;
+    }
+    const int slot = a.slot_of[(int64_t)l * a.E + e];
+    if (slot < 0 || slot >= a.S) {
+        if (flag) set_err(a.err, E0_DEV_NOT_RESIDENT);
+        return -1;
+    }
+    return slot;
+}
+
+// Gate/up rows of unit u (SHARED: the shared expert, else routed expert u):
+// hidden units 32c .. 32c + 32, written as the h block (u, c).
+template <int NP, bool SHARED>
+E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int c, float *s_small) {
+    constexpr int NB = kFuseCh / (kFuseWaves * kFlatBatch);  // batches of kFlatBatch hidden units per wavefront
+    const int lane = threadIdx.x & 63, wv = wave_id();
+    const int d = a.d, ngrp = d / kGroup;
+    const int row0 = c * kFuseCh + wv * (NB * kFlatBatch);
+    float *s_av = s_small;              // [2r] LoRA A x
+    float *s_hv = s_small + 2 * kMaxR;  // [32] h of this item
+    // x of this layer first: it does not depend on the slot.
+    uint32_t xp[NP][4][4];
+    float xs[NP], xc[NP];
+#pragma unroll
+    for (int np = 0; np < NP; ++np) {
+        xs[np] = 0.0f;
+        xc[np] = 0.0f;
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(a.x + (int64_t)l * d + (np * 64 + lane) * 32 + wd * 8);
+            x_pairs_m(v, xp[np][wd], xs[np], xc[np]);
+        }
+    }
+    const int slot = SHARED ? 0 : routed_slot(a, l, u, c == 0 && threadIdx.x == 0);
+    const bool lora = SHARED && a.r > 0;
+    if (lora) {
+        // A x of this layer, from its lora item.
+        if (!wait_ready(a.flags + l, 1, a.epoch) && threadIdx.x == 0) set_err(a.err, E0_DEV_SYNC_TIMEOUT);
+        if (threadIdx.x < 2 * a.r) s_av[threadIdx.x] = coherent_load(a.lora_a + (int64_t)l * 3 * a.r + threadIdx.x);
+        __syncthreads();
+    }
+    if (slot >= 0) {
+        u32x4 q[NB][kFlatBatch][2][NP];
+        uint32_t sbw[NB][kFlatBatch][2][NP];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const Part pq = SHARED ? a.sh.p[3 * m] : a.pool.p[3 * m];
+            const Part ps = SHARED ? a.sh.p[3 * m + 1] : a.pool.p[3 * m + 1];
+            const Part pb = SHARED ? a.sh.p[3 * m + 2] : a.pool.p[3 * m + 2];
+            const rsrc_t qr = make_rsrc(part_at(pq, l, slot), (uint32_t)a.f * d / 2);
+            const rsrc_t sr = make_rsrc(part_at(ps, l, slot), (uint32_t)a.f * ngrp * 2);
+            const rsrc_t br = make_rsrc(part_at(pb, l, slot), (uint32_t)a.f * ngrp * 2);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+                for (int rr = 0; rr < kFlatBatch; ++rr) {
+                    const uint32_t row = (uint32_t)(row0 + nb * kFlatBatch + rr);
+#pragma unroll
+                    for (int np = 0; np < NP; ++np) {
+                        const uint32_t col = (uint32_t)(np * 64 + lane);
+                        q[nb][rr][m][np] = ld128(qr, row * (d / 2) + col * 16);
+                        const uint32_t so = (row * ngrp + col / 2) * 2;
+                        sbw[nb][rr][m][np] = (uint32_t)ld16(sr, so) | ((uint32_t)ld16(br, so) << 16);
+                    }
+                }
+            }
+        }
+        const MagicConsts mk = magic_consts();
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            float acc[2 * kFlatBatch];
+#pragma unroll
+            for (int rr = 0; rr < kFlatBatch; ++rr) {
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    float v = 0.0f;
+#pragma unroll
+                    for (int np = 0; np < NP; ++np) {
+                        float dacc = 0.0f;
+#pragma unroll
+                        for (int wd = 0; wd < 4; ++wd) dacc = dot_word_m(q[nb][rr][m][np][wd], xp[np][wd], dacc, mk);
+                        const f16x2 sbv = as_h2(sbw[nb][rr][m][np]);
+                        const float sc = (float)sbv[0], bi = (float)sbv[1];
+                        v += sc * dacc + (bi * xs[np] - sc * xc[np]);
+                    }
+                    acc[m * kFlatBatch + rr] = v;
+                }
+            }
+            // 2*kFlatBatch values over 64 lanes: gate values in lanes 0..31,
+            // the matching up value in lane ^ 32.
+            group_reduce_scatter<2 * kFlatBatch, kWave>(acc);
+            constexpr int DUP = kWave / (2 * kFlatBatch);
+            const int vi = lane / DUP, m = vi / kFlatBatch, rr = vi % kFlatBatch;
+            const int row = row0 + nb * kFlatBatch + rr;
+            float val = acc[0];
+            if (lora) {
+                const uint16_t *brow = a.lb[m] + (int64_t)l * (a.lb_ls[m] / 2) + (int64_t)row * a.r;
+                float dl = 0.0f;
+                for (int i = 0; i < a.r; ++i) dl += h2f(brow[i]) * s_av[m * a.r + i];
+                val += a.lscale * dl;
+            }
+            const float other = __shfl_xor(val, 32);
+            if (m == 0 && lane % DUP == 0) s_hv[row - c * kFuseCh] = silu(val) * other;
+        }
+    } else if (threadIdx.x < kFuseCh) {
+        s_hv[threadIdx.x] = 0.0f;
+    }
+    __syncthreads();
+    // The h block of this item (wavefront 0): hi/lo fp16 pairs of h with the
+    // odd pairs scaled by 1/16, the sum and the offset sum.
+    if (threadIdx.x < 64) {
+        const int t = threadIdx.x & 31;
+        const float v = s_hv[t];
+        if (lora && threadIdx.x < kFuseCh) coherent_store(hrow(a, l, u) + c * kFuseCh + t, v);
+        const int p = t % 8, j = p % 4;
+        const float hv = (j & 1) ? v * 0.0625f : v;
+        const f16 hi = (f16)hv;
+        const f16 lo = (f16)(hv - (float)hi);
+        // pair dword (t/8)*4 + j, half p/4: gather the two halves of each dword
+        const uint32_t hbits = __builtin_bit_cast(uint16_t, hi), lbits = __builtin_bit_cast(uint16_t, lo);
+        const uint32_t hpart = __shfl_xor((int)hbits, 4), lpart = __shfl_xor((int)lbits, 4);
+        float se = (j & 1) ? 0.0f : v, so = (j & 1) ? v : 0.0f;
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) {
+            se += __shfl_xor(se, o);
+            so += __shfl_xor(so, o);
+        }
+        uint32_t *blk = hblk(a, l, u, c);
+        if (threadIdx.x < 32 && p < 4) {
+            const int dw = (t / 8) * 4 + j;
+            __hip_atomic_store(blk + dw, hbits | (hpart << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(blk + 16 + dw, lbits | (lpart << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (threadIdx.x == 0) {
+            coherent_store(reinterpret_cast<float *>(blk + kBlkSum), se + so);
+            coherent_store(reinterpret_cast<float *>(blk + kBlkCorr), 1024.0f * se + 64.0f * so);
+        }
+    }
+    signal_ready(gu_flags(a, l) + (int64_t)u * a.nch + c, a.epoch);
+}
+
+// Down rows: LPR lanes per row (d_ff = 32 * LPR), KM routed units at most
+// plus the shared expert, RW output rows per wavefront (kFuseWaves * RW per item).
+template <int LPR, int KM, int RW>
+E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, float *s_hsh, float *s_lora) {
+    constexpr int RPI = kWave / LPR;  // rows per load instruction
+    constexpr int IT = RW / RPI;      // load instructions per unit
+    static_assert(IT >= 1, "RW >= rows per load instruction");
+    const int lane = threadIdx.x & 63, wv = wave_id();
+    const int gl = lane % LPR, grp = lane / LPR;
+    const int f = a.f, d = a.d, fgrp = f / kGroup;
+    const int K = a.K;
+    const int row0 = rb * (kFuseWaves * RW) + wv * RW;
+
+    // 1. Slots of every routed unit (all scalar loads issued together), then
+    //    every weight load, before the wait.
+    int e[KM], slot[KM];
+#pragma unroll
+    for (int k = 0; k < KM; ++k) e[k] = k < K ? a.idx[(int64_t)l * K + k] : -1;
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+        slot[k] = (e[k] >= 0 && e[k] < a.E) ? a.slot_of[(int64_t)l * a.E + e[k]] : -1;
+        if (slot[k] >= a.S) slot[k] = -1;
+    }
+    u32x4 q[KM + 1][IT];
+    uint32_t sbw[KM + 1][IT];
+    auto load_unit = [&](int u, const Part &pq, const Part &ps, const Part &pb, int sl) {
+        const rsrc_t qb = make_rsrc(part_at(pq, l, sl), (uint32_t)d * f / 2);
+        const rsrc_t sb = make_rsrc(part_at(ps, l, sl), (uint32_t)d * fgrp * 2);
+        const rsrc_t bb = make_rsrc(part_at(pb, l, sl), (uint32_t)d * fgrp * 2);
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const uint32_t row = (uint32_t)(row0 + it * RPI + grp);
+            q[u][it] = ld128(qb, row * (f / 2) + gl * 16);
+            const uint32_t so = (row * fgrp + gl / 2) * 2;
+            sbw[u][it] = (uint32_t)ld16(sb, so) | ((uint32_t)ld16(bb, so) << 16);
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+        if (slot[k] >= 0) load_unit(k, a.pool.p[6], a.pool.p[7], a.pool.p[8], slot[k]);
+    if (a.has_shared) load_unit(KM, a.sh.p[6], a.sh.p[7], a.sh.p[8], 0);
+
+    // 2. Wait for the layer's gate/up items, then stage its h blocks (and the
+    //    shared expert's fp32 h for the LoRA term).
+    if (!wait_ready(gu_flags(a, l), a.units * a.nch, a.epoch) && threadIdx.x == 0) set_err(a.err, E0_DEV_SYNC_TIMEOUT);
+    const int U = a.units;
+    const uint64_t *src = reinterpret_cast<const uint64_t *>(hblk(a, l, 0, 0));
+    for (int i = threadIdx.x; i < U * LPR * (kBlk / 2); i += kFuseThreads)
+        reinterpret_cast<uint64_t *>(s_hb)[i] = coherent_load(src + i);
+    const bool lora = a.has_shared && a.r > 0;
+    if (lora)
+        for (int i = threadIdx.x; i < f; i += kFuseThreads) s_hsh[i] = coherent_load(hrow(a, l, K) + i);
+    __syncthreads();
+    if (lora) {
+        // A_down h_shared.
+        for (int i = wv; i < a.r; i += kFuseWaves) {
+            const uint16_t *arow = a.la[2] + (int64_t)l * (a.la_ls[2] / 2) + (int64_t)i * f;
+            float acc = 0.0f;
+            for (int cc = lane; cc < f; cc += kWave) acc += h2f(arow[cc]) * s_hsh[cc];
+            acc = wave_sum(acc);
+            if (lane == 0) s_lora[i] = acc;
+        }
+        __syncthreads();
+    }
+    // 3. y rows: routed units in k order, then the shared expert (weight 1).
+    const MagicConsts mk = magic_consts();
+    float acc[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) acc[it] = 0.0f;
+    auto add_unit = [&](int u, int hu, float wk) {
+        uint32_t hh[16], hlo[16];
+        const uint32_t *blk = s_hb + (hu * LPR + gl) * kBlk;
+        const u32x4 *b4 = reinterpret_cast<const u32x4 *>(blk);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 v = b4[i], w2 = b4[4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                hh[4 * i + j] = v[j];
+                hlo[4 * i + j] = w2[j];
+            }
+        }
+        const float hsum = __builtin_bit_cast(float, blk[kBlkSum]);
+        const float hcorr = __builtin_bit_cast(float, blk[kBlkCorr]);
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            float dacc = 0.0f;
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd) dacc = dot_word_m2(q[u][it][wd], hh + 4 * wd, hlo + 4 * wd, dacc, mk);
+            const f16x2 sbv = as_h2(sbw[u][it]);
+            const float sc = (float)sbv[0], bi = (float)sbv[1];
+            acc[it] += wk * (sc * dacc + (bi * hsum - sc * hcorr));
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+        if (slot[k] >= 0) add_unit(k, k, a.w[(int64_t)l * K + k]);
+    if (a.has_shared) add_unit(KM, K, 1.0f);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        float v = group_sum(acc[it], LPR);
+        const int row = row0 + it * RPI + grp;
+        if (lora) {
+            const uint16_t *brow = a.lb[2] + (int64_t)l * (a.lb_ls[2] / 2) + (int64_t)row * a.r;
+            float dl = 0.0f;
+            for (int i = 0; i < a.r; ++i) dl += h2f(brow[i]) * s_lora[i];
+            v += a.lscale * dl;
+        }
+        if (gl == 0) a.y[(int64_t)l * d + row] = v;
+    }
+}
+
+template <int NP, int LPR, int KM, int RW>
+__global__ __launch_bounds__(kFuseThreads) void decode_fused_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint32_t s_hb[(KM + 1) * LPR * kBlk];
+    __shared__ float s_hsh[32 * LPR];
+    __shared__ float s_small[2 * kMaxR + kFuseCh];
+    const int item = blockIdx.x;
+    if (item < a.n_lora) {
+        fused_lora_item(a, item);
+    } else if (item < a.n_lora + a.n_gu) {
+        const int t = item - a.n_lora;
+        const int per_l = a.units * a.nch;
+        const int l = t / per_l, u = (t % per_l) / a.nch, c = t % a.nch;
+        if (u < a.K)
+            fused_gateup_item<NP, false>(a, l, u, c, s_small);
+        else
+            fused_gateup_item<NP, true>(a, l, u, c, s_small);
+    } else {
+        const int t = item - a.n_lora - a.n_gu;
+        const int per_l = a.d / (kFuseWaves * RW);
+        fused_down_item<LPR, KM, RW>(a, t / per_l, t % per_l, s_hb, s_hsh, s_small);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -872,7 +1275,7 @@ int d_lpr(int d, int &np) {
 int f_lpr(int f) { return (f >= 128 && f <= 2048 && pow2(f)) ? f / 32 : 0; }
 
 struct Layout {
-    size_t ucnt, uexp, uslot, uoff, pairs, hbuf, lora, total;
+    size_t ucnt, uexp, uslot, uoff, pairs, hbuf, lora, flags, hblk, total;
 };
 
 Layout decode_layout(int L, int B, int K, int E, int f, int r) {
@@ -893,6 +1296,10 @@ Layout decode_layout(int L, int B, int K, int E, int f, int r) {
     off = e0_align(off + sizeof(float) * (size_t)L * (B * K + B) * f);
     o.lora = off;
     off = e0_align(off + sizeof(float) * (size_t)L * B * 3 * (r > 0 ? r : 1));
+    o.flags = off;
+    off = e0_align(off + (B == 1 ? sizeof(uint64_t) * (size_t)L * (1 + (K + 1) * (size_t)(f / kFuseCh)) : 0));
+    o.hblk = off;
+    off = e0_align(off + (B == 1 ? sizeof(uint32_t) * (size_t)L * (K + 1) * (size_t)(f / 32) * kBlk : 0));
     o.total = off;
     return o;
 }
@@ -1021,9 +1428,39 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
     a.pairs = reinterpret_cast<int32_t *>(wsb + lay.pairs);
     a.hbuf = reinterpret_cast<float *>(wsb + lay.hbuf);
     a.lora_a = reinterpret_cast<float *>(wsb + lay.lora);
+    a.flags = reinterpret_cast<uint64_t *>(wsb + lay.flags);
+    a.hblk = reinterpret_cast<uint32_t *>(wsb + lay.hblk);
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     e0_status s;
+    const int U = K + (a.has_shared ? 1 : 0);
+    if (B == 1 && lpr_d == 64 && np == 1 && (lpr_f == 8 || lpr_f == 16 || (lpr_f == 32 && K <= 4)) && K <= 8) {
+        // Batch 1, d_model 2048: the single-launch kernel.
+        a.epoch = e0_next_epoch();
+        a.units = U;
+        a.nch = f / kFuseCh;
+        a.n_lora = (a.has_shared && r > 0) ? L : 0;
+        const bool small = K <= 4;
+        const int rw = small ? 16 : 8;  // output rows per wavefront of a down item
+        const int64_t n_gu = (int64_t)L * U * a.nch, n_dn = (int64_t)L * (d / (kFuseWaves * rw));
+        E0_REQUIRE(a.n_lora + n_gu + n_dn <= (int64_t)INT32_MAX, E0_ERR_CAPACITY);
+        a.n_gu = (int)n_gu;
+        const dim3 grid((unsigned)(a.n_lora + n_gu + n_dn));
+        switch (lpr_f) {
+            case 8:
+                if (small) hipLaunchKernelGGL((decode_fused_kernel<1, 8, 4, 16>), grid, dim3(kFuseThreads), 0, st, a);
+                else hipLaunchKernelGGL((decode_fused_kernel<1, 8, 8, 8>), grid, dim3(kFuseThreads), 0, st, a);
+                break;
+            case 16:
+                if (small) hipLaunchKernelGGL((decode_fused_kernel<1, 16, 4, 16>), grid, dim3(kFuseThreads), 0, st, a);
+                else hipLaunchKernelGGL((decode_fused_kernel<1, 16, 8, 8>), grid, dim3(kFuseThreads), 0, st, a);
+                break;
+            default:
+                hipLaunchKernelGGL((decode_fused_kernel<1, 32, 4, 16>), grid, dim3(kFuseThreads), 0, st, a);
+                break;
+        }
+        return e0_launch_status();
+    }
     if (a.has_plan) {
         hipLaunchKernelGGL(decode_prep_kernel, dim3(L), dim3(kThreads), 0, st, a);
         if ((s = e0_launch_status())) return s;
@@ -1035,7 +1472,6 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
     }
     if (B == 1 && lpr_d == 64) {
         // Batch 1 at d_model = 2048 * NP: the flat one-round kernels.
-        const int U = K + (a.has_shared ? 1 : 0);
         const int64_t gu_waves = ((int64_t)L * U * f) / kFlatRows;
         const int64_t dn_waves = ((int64_t)L * d) / kFlatRows;
         E0_REQUIRE(gu_waves <= (int64_t)INT32_MAX && dn_waves <= (int64_t)INT32_MAX, E0_ERR_CAPACITY);

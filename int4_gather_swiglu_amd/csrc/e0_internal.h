@@ -114,6 +114,55 @@ E0_DEV void set_err(int32_t *err, int bits) {
     if (err) atomicOr(err, bits);
 }
 
+// ---------------------------------------------------------------------------
+// Hand-off between workgroups of one launch. A producer workgroup publishes
+// values with device-coherent stores, waits until they have completed, and
+// then stores the call's epoch into its flag; a consumer workgroup (always at
+// a higher blockIdx than its producers, and workgroups are dispatched in
+// blockIdx order, so every producer it waits for has started) polls the flags
+// with device-coherent loads and then reads the values with device-coherent
+// loads. Device-coherent accesses go to the coherence point shared by all
+// XCDs, so no cache write-back or invalidate is needed. Flags hold a 64-bit
+// epoch unique to each call, so they never need clearing. The wait is bounded
+// (kSpinTicks of the 100 MHz wall clock); on expiry it reports failure.
+// ---------------------------------------------------------------------------
+constexpr uint64_t kSpinTicks = 5000000;  // 50 ms
+
+E0_DEV void coherent_store(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+E0_DEV float coherent_load(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+E0_DEV uint64_t coherent_load(const uint64_t *p) {
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every thread of the workgroup calls this after its last coherent store.
+E0_DEV void signal_ready(uint64_t *flag, uint64_t epoch) {
+    __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every thread of the workgroup calls this; true when flags[0, n) all hold
+// `epoch`, false if the bounded wait expired. Ends with a workgroup barrier.
+E0_DEV bool wait_ready(const uint64_t *flags, int n, uint64_t epoch) {
+    int ok = 1;
+    const uint64_t t0 = wall_clock64();
+    for (int i = threadIdx.x; i < n && ok; i += blockDim.x) {
+        while (coherent_load(flags + i) != epoch) {
+            if (wall_clock64() - t0 > kSpinTicks) {
+                ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    return __syncthreads_and(ok) != 0;
+}
+
+// A per-call epoch for the flags above (never 0, distinct for 2^64 calls).
+uint64_t e0_next_epoch();
+
 // Status plumbing for host entry points.
 #define E0_REQUIRE(cond, code) \
     do {                       \
