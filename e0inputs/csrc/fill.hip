@@ -8,6 +8,9 @@
 //   codes : two little-endian uint32 words per 64-bit draw
 //   scale : fp16(0.005f + 0.015f * u),   u = (draw >> 40) * 2^-24
 //   bias  : fp16(-8 * (s * (1 + (0.2f * v - 0.1f)))), v likewise, s the fp16 scale
+// Scale/bias draw r*(cols/64) + g belongs to row r, group g; the bundle stores
+// scales and biases group-major ([cols/64][rows]), so bundle element g*rows + r
+// takes that draw.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -42,6 +45,8 @@ struct FillArgs {
     const uint64_t *keys;  // [n][3 matrices][3 parts]
     int64_t part_units[9];
     int64_t part_end[9];
+    int64_t rows[3];  // rows of gate, up, down
+    int64_t ngrp[3];  // groups per row (cols / 64)
 };
 
 __global__ __launch_bounds__(256) void fill_kernel(FillArgs a) {
@@ -60,8 +65,9 @@ __global__ __launch_bounds__(256) void fill_kernel(FillArgs a) {
     } else {
         uint16_t h[8];
         for (int i = 0; i < 8; ++i) {
-            const uint64_t g = 8 * off + i;
-            h[i] = kind == 1 ? scale_at(k[1], g) : bias_at(k[1], k[2], g);
+            const int64_t p = 8 * off + i;  // group-major position: g * rows + r
+            const uint64_t idx = (uint64_t)((p % a.rows[m]) * a.ngrp[m] + p / a.rows[m]);
+            h[i] = kind == 1 ? scale_at(k[1], idx) : bias_at(k[1], k[2], idx);
         }
         v = u32x4{h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16, h[4] | (uint32_t)h[5] << 16,
                   h[6] | (uint32_t)h[7] << 16};
@@ -86,6 +92,10 @@ extern "C" int e0gen_fill_experts(void *dst, int64_t stride, const uint64_t *key
         a.part_units[j] = (j % 3 == 0 ? qb : sb) / 16;
         acc += a.part_units[j];
         a.part_end[j] = acc;
+    }
+    for (int m = 0; m < 3; ++m) {
+        a.rows[m] = m < 2 ? f : d;
+        a.ngrp[m] = (m < 2 ? d : f) / 64;
     }
     if (stride < acc * 16 || (stride & 15) || (reinterpret_cast<uintptr_t>(dst) & 15)) return 1;
     if (n_experts == 0) return 0;

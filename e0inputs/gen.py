@@ -145,8 +145,10 @@ def expert(seed: int, layer: int, expert_id: int, d: int, f: int, tag: int = TAG
 # ---------------------------------------------------------------------------
 # Bundle layout: one expert = 9 contiguous parts
 #   [gate q | gate s | gate b | up q | up s | up b | down q | down s | down b]
-# q parts are uint32 words (8 codes each, code c at bits 4*(c%8) of word c/8),
-# s and b parts are fp16 bit patterns, groups of 64 along each row.
+# q parts are uint32 words [rows][cols/8] (8 codes each, code c at bits
+# 4*(c%8) of word c/8); s and b parts are fp16 bit patterns stored group-major,
+# [cols/64][rows]: the scale of row r, group g (columns 64g .. 64g+63) is
+# element g*rows + r. The arrays returned by quant_matrix are [rows][cols/64].
 # ---------------------------------------------------------------------------
 
 def part_sizes(d: int, f: int):
@@ -173,7 +175,7 @@ def pack_bundle(mats, d: int, f: int) -> np.ndarray:
     offs = part_offsets(d, f)
     j = 0
     for (q, s, b) in mats:
-        for arr in (q, s, b):
+        for arr in (q, s.T, b.T):
             raw = np.ascontiguousarray(arr).view(np.uint8).ravel()
             out[offs[j]:offs[j] + raw.size] = raw
             j += 1
@@ -188,9 +190,9 @@ def unpack_bundle(buf: np.ndarray, d: int, f: int):
     for m in range(3):
         rows, cols = (f, d) if m < 2 else (d, f)
         q = buf[offs[3 * m]:offs[3 * m] + sizes[3 * m]].view(np.uint32).reshape(rows, cols // 8)
-        s = buf[offs[3 * m + 1]:offs[3 * m + 1] + sizes[3 * m + 1]].view(np.uint16).reshape(rows, cols // GROUP)
-        b = buf[offs[3 * m + 2]:offs[3 * m + 2] + sizes[3 * m + 2]].view(np.uint16).reshape(rows, cols // GROUP)
-        mats.append((q, s, b))
+        s = buf[offs[3 * m + 1]:offs[3 * m + 1] + sizes[3 * m + 1]].view(np.uint16).reshape(cols // GROUP, rows)
+        b = buf[offs[3 * m + 2]:offs[3 * m + 2] + sizes[3 * m + 2]].view(np.uint16).reshape(cols // GROUP, rows)
+        mats.append((q, np.ascontiguousarray(s.T), np.ascontiguousarray(b.T)))
     return mats
 
 

@@ -28,8 +28,10 @@
  *  - int4 group-64 matrix W[rows][cols] (koala.ai.kr "two tiers" table: int4
  *    affine g64; discuss.pytorch.kr streaming section: 4-bit affine, group
  *    size 64): codes q as uint32 words [rows][cols/8], code c of a row at bits
- *    4*(c%8) of word c/8; scales s and biases b fp16 [rows][cols/64];
- *    W[r][c] = s[r][c/64] * q + b[r][c/64]. Groups run along the input
+ *    4*(c%8) of word c/8; scales s and biases b fp16, stored group-major as
+ *    [cols/64][rows] (the scale of row r, group g at element g*rows + r, so a
+ *    run of consecutive rows of one group is contiguous);
+ *    W[r][c] = s(r, c/64) * q + b(r, c/64). Groups run along the input
  *    (reduction) dimension. gate and up are [d_ff][d_model], down is
  *    [d_model][d_ff].
  */

@@ -250,14 +250,11 @@ E0_DEV void x_pairs(const u32x4 v, uint32_t (&o)[4]) {
     o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
 }
 
-// (a & m) | c in one v_and_or_b32. gfx9 VOP3 instructions take at most one
-// scalar or literal operand, so the two constants live in VGPRs (held by the
-// caller) and the instruction is spelled out.
-E0_DEV uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-    uint32_t r;
-    __asm__("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
-    return r;
-}
+// (a & m) | c, selected as one v_and_or_b32. gfx9 VOP3 instructions take at
+// most one scalar or literal operand, so the two constants live in VGPRs:
+// the callers take them from nibble_consts() / magic_consts(), whose values
+// the compiler cannot see, which keeps it from splitting the operation.
+E0_DEV uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) { return (a & m) | c; }
 
 // Constants of the nibble-to-fp16 placement, kept in VGPRs.
 struct NibbleConsts {
@@ -474,8 +471,8 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
                         const uint32_t col = (uint32_t)(np * LPR + gl);  // 32-element column block
                         const uint32_t g = col / 2;                           // its group
                         qv[rr][m][np] = ld128(qr[m], (uint32_t)row * (d / 2) + col * 16);
-                        sv[rr][m][np] = h2f(ld16(sr[m], ((uint32_t)row * ngrp + g) * 2));
-                        bv[rr][m][np] = h2f(ld16(br[m], ((uint32_t)row * ngrp + g) * 2));
+                        sv[rr][m][np] = h2f(ld16(sr[m], (g * (uint32_t)a.f + (uint32_t)row) * 2));
+                        bv[rr][m][np] = h2f(ld16(br[m], (g * (uint32_t)a.f + (uint32_t)row) * 2));
                     }
                 }
             }
@@ -610,8 +607,8 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(DecodeArgs a) {
         for (int it = 0; it < IT; ++it) {
             const uint32_t row = (uint32_t)min(rows[it], d - 1);  // clamped: in-bounds, never written
             const u32x4 qv = ld128(qb, row * (f / 2) + gl * 16);
-            const float s = h2f(ld16(sb, (row * fgrp + g) * 2));
-            const float b = h2f(ld16(bb, (row * fgrp + g) * 2));
+            const float s = h2f(ld16(sb, ((uint32_t)g * d + row) * 2));
+            const float b = h2f(ld16(bb, ((uint32_t)g * d + row) * 2));
             out[it] += wk * down_dot(qv, s, b, h, hsum);
         }
     };
@@ -789,7 +786,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_flat_kernel(DecodeArgs
                 for (int np = 0; np < NP; ++np) {
                     const uint32_t col = (uint32_t)(np * 64 + lane);
                     B.q[rr][m][np] = ld128(qr[m], row * (d / 2) + col * 16);
-                    const uint32_t so = (row * ngrp + col / 2) * 2;
+                    const uint32_t so = ((col / 2) * (uint32_t)a.f + row) * 2;
                     B.sb[rr][m][np] = (uint32_t)ld16(sr[m], so) | ((uint32_t)ld16(br[m], so) << 16);
                 }
             }
@@ -891,8 +888,8 @@ __global__ __launch_bounds__(kThreads) void decode_down_flat_kernel(DecodeArgs a
         for (int it = 0; it < IT; ++it) {
             const uint32_t row = (uint32_t)(row0 + it * RPI + grp);
             qv[it] = ld128(qb, row * (f / 2) + gl * 16);
-            sv[it] = h2f(ld16(sb, (row * fgrp + g) * 2));
-            bv[it] = h2f(ld16(bb, (row * fgrp + g) * 2));
+            sv[it] = h2f(ld16(sb, ((uint32_t)g * d + row) * 2));
+            bv[it] = h2f(ld16(bb, ((uint32_t)g * d + row) * 2));
         }
         const float *hp = hrow(a, l, u) + col0;
         float h[32];
@@ -971,20 +968,22 @@ E0_DEV void fused_lora_item(const DecodeArgs &a, int l) {
     signal_ready(a.flags + l, a.epoch);
 }
 
-// Slot of routed expert k of layer l (batch 1), or -1 (flagging the error
-// when `flag`).
-E0_DEV int routed_slot(const DecodeArgs &a, int l, int k, bool flag) {
+// Slot of routed expert k of layer l (batch 1), or -1 with the reason in
+// `bits` (E0_DEV_BAD_ID / E0_DEV_NOT_RESIDENT). The result is wave-uniform.
+E0_DEV int routed_slot(const DecodeArgs &a, int l, int k, int &bits) {
     const int e = a.idx[(int64_t)l * a.K + k];
+    int slot = -1;
+    bits = 0;
     if (e < 0 || e >= a.E) {
-        if (flag) set_err(a.err, E0_DEV_BAD_ID);
-        return -1;
+        bits = E0_DEV_BAD_ID;
+    } else {
+        slot = a.slot_of[(int64_t)l * a.E + e];
+        if (slot < 0 || slot >= a.S) {
+            bits = E0_DEV_NOT_RESIDENT;
+            slot = -1;
+        }
     }
-    const int slot = a.slot_of[(int64_t)l * a.E + e];
-    if (slot < 0 || slot >= a.S) {
-        if (flag) set_err(a.err, E0_DEV_NOT_RESIDENT);
-        return -1;
-    }
-    return slot;
+    return __builtin_amdgcn_readfirstlane(slot);
 }
 
 // Gate/up rows of unit u (SHARED: the shared expert, else routed expert u):
@@ -1010,7 +1009,9 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int c, float *s
             x_pairs_m(v, xp[np][wd], xs[np], xc[np]);
         }
     }
-    const int slot = SHARED ? 0 : routed_slot(a, l, u, c == 0 && threadIdx.x == 0);
+    int bits = 0;
+    const int slot = SHARED ? 0 : routed_slot(a, l, u, bits);
+    if (bits && c == 0 && threadIdx.x == 0) set_err(a.err, bits);
     const bool lora = SHARED && a.r > 0;
     if (lora) {
         // A x of this layer, from its lora item.
@@ -1020,7 +1021,10 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int c, float *s
     }
     if (slot >= 0) {
         u32x4 q[NB][kFlatBatch][2][NP];
-        uint32_t sbw[NB][kFlatBatch][2][NP];
+        // Scales and biases are group-major, so the 8 consecutive rows of this
+        // wavefront and the lane's group are 16 contiguous bytes each.
+        static_assert(NB * kFlatBatch == 8, "one 16-byte scale load covers the wavefront's rows");
+        u32x4 sv[2][NP], bv[2][NP];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const Part pq = SHARED ? a.sh.p[3 * m] : a.pool.p[3 * m];
@@ -1030,6 +1034,12 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int c, float *s
             const rsrc_t sr = make_rsrc(part_at(ps, l, slot), (uint32_t)a.f * ngrp * 2);
             const rsrc_t br = make_rsrc(part_at(pb, l, slot), (uint32_t)a.f * ngrp * 2);
 #pragma unroll
+            for (int np = 0; np < NP; ++np) {
+                const uint32_t g = (uint32_t)(np * 64 + lane) / 2;
+                sv[m][np] = ld128(sr, (g * (uint32_t)a.f + (uint32_t)row0) * 2);
+                bv[m][np] = ld128(br, (g * (uint32_t)a.f + (uint32_t)row0) * 2);
+            }
+#pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
                 for (int rr = 0; rr < kFlatBatch; ++rr) {
@@ -1038,12 +1048,13 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int c, float *s
                     for (int np = 0; np < NP; ++np) {
                         const uint32_t col = (uint32_t)(np * 64 + lane);
                         q[nb][rr][m][np] = ld128(qr, row * (d / 2) + col * 16);
-                        const uint32_t so = (row * ngrp + col / 2) * 2;
-                        sbw[nb][rr][m][np] = (uint32_t)ld16(sr, so) | ((uint32_t)ld16(br, so) << 16);
                     }
                 }
             }
         }
+        // Every load of the item is issued before the first use (keeps the
+        // compiler from spreading them through the compute phase).
+        __asm__ __volatile__("" ::: "memory");
         const MagicConsts mk = magic_consts();
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -1058,8 +1069,9 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int c, float *s
                         float dacc = 0.0f;
 #pragma unroll
                         for (int wd = 0; wd < 4; ++wd) dacc = dot_word_m(q[nb][rr][m][np][wd], xp[np][wd], dacc, mk);
-                        const f16x2 sbv = as_h2(sbw[nb][rr][m][np]);
-                        const float sc = (float)sbv[0], bi = (float)sbv[1];
+                        const int j = nb * kFlatBatch + rr;  // row within the wavefront's 8
+                        const float sc = (float)as_h2(sv[m][np][j / 2])[j % 2];
+                        const float bi = (float)as_h2(bv[m][np][j / 2])[j % 2];
                         v += sc * dacc + (bi * xs[np] - sc * xc[np]);
                     }
                     acc[m * kFlatBatch + rr] = v;
@@ -1134,39 +1146,76 @@ E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, 
     // 1. Slots of every routed unit (all scalar loads issued together), then
     //    every weight load, before the wait.
     int e[KM], slot[KM];
+    float wk[KM];
 #pragma unroll
-    for (int k = 0; k < KM; ++k) e[k] = k < K ? a.idx[(int64_t)l * K + k] : -1;
+    for (int k = 0; k < KM; ++k) {
+        e[k] = k < K ? a.idx[(int64_t)l * K + k] : -1;
+        wk[k] = k < K ? a.w[(int64_t)l * K + k] : 0.0f;
+    }
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
         slot[k] = (e[k] >= 0 && e[k] < a.E) ? a.slot_of[(int64_t)l * a.E + e[k]] : -1;
         if (slot[k] >= a.S) slot[k] = -1;
     }
+    // Loads are issued without branches (a branch around a load makes the
+    // compiler wait for it at the join): a unit that does not exist or has
+    // no valid slot reads through a zero-size buffer descriptor, which returns
+    // zeros without touching memory, and contributes nothing. Lane group grp
+    // owns IT consecutive rows, so its group-major scales (and biases) are
+    // 2 * IT contiguous bytes.
+    static_assert(IT == 2 || IT == 4 || IT == 8, "scale loads of 4, 8 or 16 bytes");
     u32x4 q[KM + 1][IT];
-    uint32_t sbw[KM + 1][IT];
-    auto load_unit = [&](int u, const Part &pq, const Part &ps, const Part &pb, int sl) {
-        const rsrc_t qb = make_rsrc(part_at(pq, l, sl), (uint32_t)d * f / 2);
-        const rsrc_t sb = make_rsrc(part_at(ps, l, sl), (uint32_t)d * fgrp * 2);
-        const rsrc_t bb = make_rsrc(part_at(pb, l, sl), (uint32_t)d * fgrp * 2);
+    uint32_t sv[KM + 1][IT / 2], bv[KM + 1][IT / 2];
+    auto load_halves = [&](const rsrc_t &r, uint32_t off, uint32_t (&o)[IT / 2]) {
+        if constexpr (IT == 2) {
+            o[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+        } else if constexpr (IT == 4) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+            o[0] = v[0];
+            o[1] = v[1];
+        } else {
+            const u32x4 v = ld128(r, off);
 #pragma unroll
-        for (int it = 0; it < IT; ++it) {
-            const uint32_t row = (uint32_t)(row0 + it * RPI + grp);
-            q[u][it] = ld128(qb, row * (f / 2) + gl * 16);
-            const uint32_t so = (row * fgrp + gl / 2) * 2;
-            sbw[u][it] = (uint32_t)ld16(sb, so) | ((uint32_t)ld16(bb, so) << 16);
+            for (int j = 0; j < 4; ++j) o[j] = v[j];
         }
     };
+    const int rows0 = row0 + grp * IT;  // this lane group's first row
+    auto load_unit = [&](int u, const Part &pq, const Part &ps, const Part &pb, int sl, bool on) {
+        const int s0 = on ? sl : 0;
+        const rsrc_t qb = make_rsrc(part_at(pq, l, s0), on ? (uint32_t)d * f / 2 : 0u);
+        const rsrc_t sb = make_rsrc(part_at(ps, l, s0), on ? (uint32_t)d * fgrp * 2 : 0u);
+        const rsrc_t bb = make_rsrc(part_at(pb, l, s0), on ? (uint32_t)d * fgrp * 2 : 0u);
 #pragma unroll
-    for (int k = 0; k < KM; ++k)
-        if (slot[k] >= 0) load_unit(k, a.pool.p[6], a.pool.p[7], a.pool.p[8], slot[k]);
-    if (a.has_shared) load_unit(KM, a.sh.p[6], a.sh.p[7], a.sh.p[8], 0);
+        for (int it = 0; it < IT; ++it) q[u][it] = ld128(qb, (uint32_t)(rows0 + it) * (f / 2) + gl * 16);
+        const uint32_t so = ((uint32_t)(gl / 2) * d + (uint32_t)rows0) * 2;
+        load_halves(sb, so, sv[u]);
+        load_halves(bb, so, bv[u]);
+    };
+#pragma unroll
+    for (int k = 0; k < KM; ++k) load_unit(k, a.pool.p[6], a.pool.p[7], a.pool.p[8], slot[k], slot[k] >= 0);
+    load_unit(KM, a.sh.p[6], a.sh.p[7], a.sh.p[8], 0, a.has_shared != 0);
 
     // 2. Wait for the layer's gate/up items, then stage its h blocks (and the
     //    shared expert's fp32 h for the LoRA term).
     if (!wait_ready(gu_flags(a, l), a.units * a.nch, a.epoch) && threadIdx.x == 0) set_err(a.err, E0_DEV_SYNC_TIMEOUT);
     const int U = a.units;
-    const uint64_t *src = reinterpret_cast<const uint64_t *>(hblk(a, l, 0, 0));
-    for (int i = threadIdx.x; i < U * LPR * (kBlk / 2); i += kFuseThreads)
-        reinterpret_cast<uint64_t *>(s_hb)[i] = coherent_load(src + i);
+    {
+        // All staging loads in flight at once, then the LDS writes.
+        constexpr int kMaxStage = ((KM + 1) * LPR * (kBlk / 2) + kFuseThreads - 1) / kFuseThreads;
+        const int n = U * LPR * (kBlk / 2);
+        const uint64_t *src = reinterpret_cast<const uint64_t *>(hblk(a, l, 0, 0));
+        uint64_t tmp[kMaxStage];
+#pragma unroll
+        for (int j = 0; j < kMaxStage; ++j) {
+            const int i = threadIdx.x + j * kFuseThreads;
+            tmp[j] = i < n ? coherent_load(src + i) : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < kMaxStage; ++j) {
+            const int i = threadIdx.x + j * kFuseThreads;
+            if (i < n) reinterpret_cast<uint64_t *>(s_hb)[i] = tmp[j];
+        }
+    }
     const bool lora = a.has_shared && a.r > 0;
     if (lora)
         for (int i = threadIdx.x; i < f; i += kFuseThreads) s_hsh[i] = coherent_load(hrow(a, l, K) + i);
@@ -1207,19 +1256,18 @@ E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, 
             float dacc = 0.0f;
 #pragma unroll
             for (int wd = 0; wd < 4; ++wd) dacc = dot_word_m2(q[u][it][wd], hh + 4 * wd, hlo + 4 * wd, dacc, mk);
-            const f16x2 sbv = as_h2(sbw[u][it]);
-            const float sc = (float)sbv[0], bi = (float)sbv[1];
+            const float sc = (float)as_h2(sv[u][it / 2])[it % 2], bi = (float)as_h2(bv[u][it / 2])[it % 2];
             acc[it] += wk * (sc * dacc + (bi * hsum - sc * hcorr));
         }
     };
 #pragma unroll
     for (int k = 0; k < KM; ++k)
-        if (slot[k] >= 0) add_unit(k, k, a.w[(int64_t)l * K + k]);
+        if (slot[k] >= 0) add_unit(k, k, wk[k]);
     if (a.has_shared) add_unit(KM, K, 1.0f);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         float v = group_sum(acc[it], LPR);
-        const int row = row0 + it * RPI + grp;
+        const int row = rows0 + it;
         if (lora) {
             const uint16_t *brow = a.lb[2] + (int64_t)l * (a.lb_ls[2] / 2) + (int64_t)row * a.r;
             float dl = 0.0f;
@@ -1441,7 +1489,9 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
         a.nch = f / kFuseCh;
         a.n_lora = (a.has_shared && r > 0) ? L : 0;
         const bool small = K <= 4;
-        const int rw = small ? 16 : 8;  // output rows per wavefront of a down item
+        // output rows per wavefront of a down item (at least two load
+        // instructions per unit, so its scales are one 4/8/16-byte load)
+        const int rw = (small || lpr_f == 8) ? 16 : 8;
         const int64_t n_gu = (int64_t)L * U * a.nch, n_dn = (int64_t)L * (d / (kFuseWaves * rw));
         E0_REQUIRE(a.n_lora + n_gu + n_dn <= (int64_t)INT32_MAX, E0_ERR_CAPACITY);
         a.n_gu = (int)n_gu;
@@ -1449,7 +1499,7 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
         switch (lpr_f) {
             case 8:
                 if (small) hipLaunchKernelGGL((decode_fused_kernel<1, 8, 4, 16>), grid, dim3(kFuseThreads), 0, st, a);
-                else hipLaunchKernelGGL((decode_fused_kernel<1, 8, 8, 8>), grid, dim3(kFuseThreads), 0, st, a);
+                else hipLaunchKernelGGL((decode_fused_kernel<1, 8, 8, 16>), grid, dim3(kFuseThreads), 0, st, a);
                 break;
             case 16:
                 if (small) hipLaunchKernelGGL((decode_fused_kernel<1, 16, 4, 16>), grid, dim3(kFuseThreads), 0, st, a);
