@@ -9,8 +9,8 @@
 //   scale : fp16(0.005f + 0.015f * u),   u = (draw >> 40) * 2^-24
 //   bias  : fp16(-8 * (s * (1 + (0.2f * v - 0.1f)))), v likewise, s the fp16 scale
 // Scale/bias draw r*(cols/64) + g belongs to row r, group g; the bundle stores
-// scales and biases group-major ([cols/64][rows]), so bundle element g*rows + r
-// takes that draw.
+// scales and biases in tiles of 8 rows ([rows/8][cols/64][8]), so bundle
+// element ((r/8)*(cols/64) + g)*8 + r%8 takes that draw.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -65,8 +65,9 @@ __global__ __launch_bounds__(256) void fill_kernel(FillArgs a) {
     } else {
         uint16_t h[8];
         for (int i = 0; i < 8; ++i) {
-            const int64_t p = 8 * off + i;  // group-major position: g * rows + r
-            const uint64_t idx = (uint64_t)((p % a.rows[m]) * a.ngrp[m] + p / a.rows[m]);
+            const int64_t p = 8 * off + i;  // tiled position ((r/8)*ngrp + g)*8 + r%8
+            const int64_t r = (p / (8 * a.ngrp[m])) * 8 + p % 8, g = (p / 8) % a.ngrp[m];
+            const uint64_t idx = (uint64_t)(r * a.ngrp[m] + g);
             h[i] = kind == 1 ? scale_at(k[1], idx) : bias_at(k[1], k[2], idx);
         }
         v = u32x4{h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16, h[4] | (uint32_t)h[5] << 16,

@@ -146,9 +146,11 @@ def expert(seed: int, layer: int, expert_id: int, d: int, f: int, tag: int = TAG
 # Bundle layout: one expert = 9 contiguous parts
 #   [gate q | gate s | gate b | up q | up s | up b | down q | down s | down b]
 # q parts are uint32 words [rows][cols/8] (8 codes each, code c at bits
-# 4*(c%8) of word c/8); s and b parts are fp16 bit patterns stored group-major,
-# [cols/64][rows]: the scale of row r, group g (columns 64g .. 64g+63) is
-# element g*rows + r. The arrays returned by quant_matrix are [rows][cols/64].
+# 4*(c%8) of word c/8); s and b parts are fp16 bit patterns stored in tiles of
+# 8 rows, [rows/8][cols/64][8]: the scale of row r, group g (columns 64g ..
+# 64g+63) is element ((r/8)*(cols/64) + g)*8 + r%8, so the 8 rows of a tile in
+# one group are 16 contiguous bytes and a tile's groups follow each other.
+# The arrays returned by quant_matrix are [rows][cols/64].
 # ---------------------------------------------------------------------------
 
 def part_sizes(d: int, f: int):
@@ -169,13 +171,23 @@ def bundle_bytes(d: int, f: int) -> int:
     return sum(part_sizes(d, f))
 
 
+def _tile8(a: np.ndarray) -> np.ndarray:
+    """[rows][ngrp] -> [rows/8][ngrp][8] (the bundle order of scales and biases)."""
+    rows, ngrp = a.shape
+    return a.reshape(rows // 8, 8, ngrp).transpose(0, 2, 1)
+
+
+def _untile8(flat: np.ndarray, rows: int, ngrp: int) -> np.ndarray:
+    return np.ascontiguousarray(flat.reshape(rows // 8, ngrp, 8).transpose(0, 2, 1).reshape(rows, ngrp))
+
+
 def pack_bundle(mats, d: int, f: int) -> np.ndarray:
     """uint8 bundle of one expert from [(q, s, b)] * 3."""
     out = np.empty(bundle_bytes(d, f), dtype=np.uint8)
     offs = part_offsets(d, f)
     j = 0
     for (q, s, b) in mats:
-        for arr in (q, s.T, b.T):
+        for arr in (q, _tile8(s), _tile8(b)):
             raw = np.ascontiguousarray(arr).view(np.uint8).ravel()
             out[offs[j]:offs[j] + raw.size] = raw
             j += 1
@@ -190,9 +202,9 @@ def unpack_bundle(buf: np.ndarray, d: int, f: int):
     for m in range(3):
         rows, cols = (f, d) if m < 2 else (d, f)
         q = buf[offs[3 * m]:offs[3 * m] + sizes[3 * m]].view(np.uint32).reshape(rows, cols // 8)
-        s = buf[offs[3 * m + 1]:offs[3 * m + 1] + sizes[3 * m + 1]].view(np.uint16).reshape(cols // GROUP, rows)
-        b = buf[offs[3 * m + 2]:offs[3 * m + 2] + sizes[3 * m + 2]].view(np.uint16).reshape(cols // GROUP, rows)
-        mats.append((q, np.ascontiguousarray(s.T), np.ascontiguousarray(b.T)))
+        s = buf[offs[3 * m + 1]:offs[3 * m + 1] + sizes[3 * m + 1]].view(np.uint16)
+        b = buf[offs[3 * m + 2]:offs[3 * m + 2] + sizes[3 * m + 2]].view(np.uint16)
+        mats.append((q, _untile8(s, rows, cols // GROUP), _untile8(b, rows, cols // GROUP)))
     return mats
 
 

@@ -28,9 +28,10 @@
  *  - int4 group-64 matrix W[rows][cols] (koala.ai.kr "two tiers" table: int4
  *    affine g64; discuss.pytorch.kr streaming section: 4-bit affine, group
  *    size 64): codes q as uint32 words [rows][cols/8], code c of a row at bits
- *    4*(c%8) of word c/8; scales s and biases b fp16, stored group-major as
- *    [cols/64][rows] (the scale of row r, group g at element g*rows + r, so a
- *    run of consecutive rows of one group is contiguous);
+ *    4*(c%8) of word c/8; scales s and biases b fp16, stored in tiles of 8
+ *    rows as [rows/8][cols/64][8] (the scale of row r, group g at element
+ *    ((r/8)*(cols/64) + g)*8 + r%8: a tile's 8 rows of one group are 16
+ *    contiguous bytes, and the tile's groups follow each other);
  *    W[r][c] = s(r, c/64) * q + b(r, c/64). Groups run along the input
  *    (reduction) dimension. gate and up are [d_ff][d_model], down is
  *    [d_model][d_ff].

@@ -79,9 +79,11 @@ struct DecodeArgs {
     uint64_t *flags;  // [L] lora items, then [L][units][nch] gate/up items
     uint64_t epoch;
     int units;        // K + (shared expert ? 1 : 0)
-    int nch;          // gate/up items per unit (d_ff / kFuseCh)
+    int nch;          // h half blocks (flags) per unit: d_ff / 16
     int n_lora;       // lora items (L with LoRA, else 0)
-    int n_gu;         // gate/up items (L * units * nch)
+    int n_gu;         // gate/up items per layer (units * d_ff / 64)
+    int n_dn;         // down items per layer
+    int lag;          // the down items of layer l follow the gate/up items of layer l + lag
 };
 
 E0_DEV int pairs_per_layer(const DecodeArgs &a) { return a.B * a.K + a.B; }
@@ -252,7 +254,7 @@ E0_DEV void x_pairs(const u32x4 v, uint32_t (&o)[4]) {
 
 // (a & m) | c, selected as one v_and_or_b32. gfx9 VOP3 instructions take at
 // most one scalar or literal operand, so the two constants live in VGPRs:
-// the callers take them from nibble_consts() / magic_consts(), whose values
+// the callers take them from nibble_consts(), whose values
 // the compiler cannot see, which keeps it from splitting the operation.
 E0_DEV uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) { return (a & m) | c; }
 
@@ -282,39 +284,30 @@ E0_DEV float dot_word(uint32_t w, const uint32_t (&xp)[4], float acc, NibbleCons
 }
 E0_DEV float dot_word(uint32_t w, const uint32_t (&xp)[4], float acc) { return dot_word(w, xp, acc, nibble_consts()); }
 
-// Nibble placement with a 1024 offset, no shifts for half of the codes:
-// (w & m) | 0x64006400 gives, per fp16 half, 1024 + q for a nibble at bits
-// 0..3 of the half and 1024 + 16 q for a nibble at bits 4..7 (exact).
-struct MagicConsts {
-    uint32_t lo, hi, one;
-};
-E0_DEV MagicConsts magic_consts() {
-    MagicConsts k;
-    __asm__("v_mov_b32 %0, 0x000f000f" : "=v"(k.lo));
-    __asm__("v_mov_b32 %0, 0x00f000f0" : "=v"(k.hi));
-    __asm__("v_mov_b32 %0, 0x64006400" : "=v"(k.one));
-    return k;
-}
+// Nibbles as fp16 denormals: w & 0x000F000F puts the codes at bits 0..3 of
+// each half, which read as fp16 are q * 2^-24; w & 0x00F000F0 (bits 4..7)
+// reads as q * 2^-20. v_dot2_f32_f16 takes denormal inputs exactly, so with
+// the inputs v of the second kind pre-scaled by 1/16 every product is
+// q * v * 2^-24, exact in fp32. One shift, four single-source ANDs (full rate,
+// unlike a three-register and-or) and four dot2 per 8 codes.
+constexpr float kDenormScale = 16777216.0f;  // 2^24
 
-// Over the 8 codes of `w`: sum of (1024 + q_c) v_c for c in {0, 2, 4, 6} and
-// (1024 + 16 q_c) (v_c / 16) for c in {1, 3, 5, 7}, with v given as the pairs
-// (v0, v4), (v1/16, v5/16), (v2, v6), (v3/16, v7/16). The result is
-// sum(q v) + 1024 (v0 + v2 + v4 + v6) + 64 (v1 + v3 + v5 + v7).
-E0_DEV float dot_word_m(uint32_t w, const uint32_t *vp, float acc, MagicConsts k) {
+// Over the 8 codes of `w`: 2^-24 * sum(q_c v_c), v given as the pairs
+// (v0, v4), (v1/16, v5/16), (v2, v6), (v3/16, v7/16).
+E0_DEV float dot_word_m(uint32_t w, const uint32_t *vp, float acc) {
     const uint32_t w8 = w >> 8;
-    acc = __builtin_amdgcn_fdot2(as_h2(and_or(w, k.lo, k.one)), as_h2(vp[0]), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_h2(and_or(w, k.hi, k.one)), as_h2(vp[1]), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_h2(and_or(w8, k.lo, k.one)), as_h2(vp[2]), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_h2(and_or(w8, k.hi, k.one)), as_h2(vp[3]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(w & 0x000F000Fu), as_h2(vp[0]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(w & 0x00F000F0u), as_h2(vp[1]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(w8 & 0x000F000Fu), as_h2(vp[2]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(w8 & 0x00F000F0u), as_h2(vp[3]), acc, false);
     return acc;
 }
 
 // The same with v split in two fp16 parts, vh + vl (hi = fp16(v), lo =
 // fp16(v - hi)), for fp32 inputs.
-E0_DEV float dot_word_m2(uint32_t w, const uint32_t *vh, const uint32_t *vl, float acc, MagicConsts k) {
+E0_DEV float dot_word_m2(uint32_t w, const uint32_t *vh, const uint32_t *vl, float acc) {
     const uint32_t w8 = w >> 8;
-    const uint32_t t0 = and_or(w, k.lo, k.one), t1 = and_or(w, k.hi, k.one);
-    const uint32_t t2 = and_or(w8, k.lo, k.one), t3 = and_or(w8, k.hi, k.one);
+    const uint32_t t0 = w & 0x000F000Fu, t1 = w & 0x00F000F0u, t2 = w8 & 0x000F000Fu, t3 = w8 & 0x00F000F0u;
     acc = __builtin_amdgcn_fdot2(as_h2(t0), as_h2(vh[0]), acc, false);
     acc = __builtin_amdgcn_fdot2(as_h2(t0), as_h2(vl[0]), acc, false);
     acc = __builtin_amdgcn_fdot2(as_h2(t1), as_h2(vh[1]), acc, false);
@@ -326,25 +319,17 @@ E0_DEV float dot_word_m2(uint32_t w, const uint32_t *vh, const uint32_t *vl, flo
     return acc;
 }
 
-// Magic-offset pairs of 8 consecutive fp16 inputs (4 dwords), and their
-// plain sum and offset sum 1024 (v0 + v2 + v4 + v6) + 64 (v1 + v3 + v5 + v7).
-E0_DEV void x_pairs_m(const u32x4 v, uint32_t (&o)[4], float &sum, float &corr) {
+// Pairs (v0, v4), (v1/16, v5/16), (v2, v6), (v3/16, v7/16) of 8 consecutive
+// fp16 inputs (4 dwords), and their plain sum.
+E0_DEV void x_pairs_m(const u32x4 v, uint32_t (&o)[4], float &sum) {
     x_pairs(v, o);
     const f16x2 k16 = {(f16)0.0625f, (f16)0.0625f};
-    float se = 0.0f, so = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const f16x2 hv = as_h2(o[j]);
-        const float t = (float)hv[0] + (float)hv[1];
-        if (j & 1) {
-            so += t;
-            o[j] = __builtin_bit_cast(uint32_t, hv * k16);
-        } else {
-            se += t;
-        }
+        sum += (float)hv[0] + (float)hv[1];
+        if (j & 1) o[j] = __builtin_bit_cast(uint32_t, hv * k16);
     }
-    sum += se + so;
-    corr += 1024.0f * se + 64.0f * so;
 }
 
 // ---------------------------------------------------------------------------
@@ -471,8 +456,8 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
                         const uint32_t col = (uint32_t)(np * LPR + gl);  // 32-element column block
                         const uint32_t g = col / 2;                           // its group
                         qv[rr][m][np] = ld128(qr[m], (uint32_t)row * (d / 2) + col * 16);
-                        sv[rr][m][np] = h2f(ld16(sr[m], (g * (uint32_t)a.f + (uint32_t)row) * 2));
-                        bv[rr][m][np] = h2f(ld16(br[m], (g * (uint32_t)a.f + (uint32_t)row) * 2));
+                        sv[rr][m][np] = h2f(ld16(sr[m], sb_index((uint32_t)row, g, ngrp) * 2));
+                        bv[rr][m][np] = h2f(ld16(br[m], sb_index((uint32_t)row, g, ngrp) * 2));
                     }
                 }
             }
@@ -607,8 +592,8 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(DecodeArgs a) {
         for (int it = 0; it < IT; ++it) {
             const uint32_t row = (uint32_t)min(rows[it], d - 1);  // clamped: in-bounds, never written
             const u32x4 qv = ld128(qb, row * (f / 2) + gl * 16);
-            const float s = h2f(ld16(sb, ((uint32_t)g * d + row) * 2));
-            const float b = h2f(ld16(bb, ((uint32_t)g * d + row) * 2));
+            const float s = h2f(ld16(sb, sb_index(row, (uint32_t)g, (uint32_t)fgrp) * 2));
+            const float b = h2f(ld16(bb, sb_index(row, (uint32_t)g, (uint32_t)fgrp) * 2));
             out[it] += wk * down_dot(qv, s, b, h, hsum);
         }
     };
@@ -786,7 +771,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_flat_kernel(DecodeArgs
                 for (int np = 0; np < NP; ++np) {
                     const uint32_t col = (uint32_t)(np * 64 + lane);
                     B.q[rr][m][np] = ld128(qr[m], row * (d / 2) + col * 16);
-                    const uint32_t so = ((col / 2) * (uint32_t)a.f + row) * 2;
+                    const uint32_t so = sb_index(row, col / 2, (uint32_t)ngrp) * 2;
                     B.sb[rr][m][np] = (uint32_t)ld16(sr[m], so) | ((uint32_t)ld16(br[m], so) << 16);
                 }
             }
@@ -888,8 +873,8 @@ __global__ __launch_bounds__(kThreads) void decode_down_flat_kernel(DecodeArgs a
         for (int it = 0; it < IT; ++it) {
             const uint32_t row = (uint32_t)(row0 + it * RPI + grp);
             qv[it] = ld128(qb, row * (f / 2) + gl * 16);
-            sv[it] = h2f(ld16(sb, ((uint32_t)g * d + row) * 2));
-            bv[it] = h2f(ld16(bb, ((uint32_t)g * d + row) * 2));
+            sv[it] = h2f(ld16(sb, sb_index(row, (uint32_t)g, (uint32_t)fgrp) * 2));
+            bv[it] = h2f(ld16(bb, sb_index(row, (uint32_t)g, (uint32_t)fgrp) * 2));
         }
         const float *hp = hrow(a, l, u) + col0;
         float h[32];
@@ -924,22 +909,24 @@ __global__ __launch_bounds__(kThreads) void decode_down_flat_kernel(DecodeArgs a
 // ---------------------------------------------------------------------------
 // Batch-1 single-launch decode. The work of a call is one list of items, one
 // workgroup each, in blockIdx order:
-//   lora items     (l)        A_gate x and A_up x of the shared expert's LoRA
-//   gate/up items  (l, u, c)  gate and up rows c*kFuseCh .. +kFuseCh of unit u
-//                             (routed expert k = u < K, shared expert u = K):
-//                             h[l][u][rows] = silu(gate x) * up x
-//   down items     (l, rb)    a block of output rows of layer l:
-//                             y = sum over units in k order of w_u down_u h_u
+//   lora items     (l)         A_gate x and A_up x of the shared expert's LoRA
+//   gate/up items  (l, u, cg)  gate and up rows of 64 hidden units of unit u
+//                              (routed expert k = u < K, shared expert u = K):
+//                              h = silu(gate x) * up x, published per 16 units
+//   down items     (l, rb)     a block of output rows of layer l:
+//                              y = sum over units in k order of w_u down_u h_u
 // Consumers (down items; shared gate/up items with LoRA) wait for the flags
-// of their producers, which precede them in blockIdx order; a down item
-// issues its weight loads before it waits. One launch streams every weight
-// byte once with no gap between the gate/up and the down phases.
+// of their producers, which precede them in blockIdx order, and a layer's
+// down items are placed about one machine's worth of items after its gate/up
+// items, so the waits are short; a down item issues its weight loads before
+// it waits. One launch streams every weight byte once, with the down
+// projections of early layers overlapping the gate/up rows of later ones.
 // ---------------------------------------------------------------------------
-constexpr int kFuseCh = 32;      // hidden units per gate/up item (4 per wavefront)
+constexpr int kHalfBlk = 16;     // hidden units per h half block (one flag each)
 constexpr int kFuseThreads = 256;
 constexpr int kFuseWaves = kFuseThreads / kWave;
-constexpr int kBlk = 36;         // dwords per h block: 16 hi pairs, 16 lo pairs, sum, offset sum, 2 pad
-constexpr int kBlkSum = 32, kBlkCorr = 33;
+constexpr int kBlk = 36;  // dwords per h block: 16 hi pairs, 16 lo pairs, the sum of each half (+ pad)
+constexpr int kBlkSum = 32;
 
 E0_DEV uint64_t *gu_flags(const DecodeArgs &a, int l) { return a.flags + a.L + (int64_t)l * a.units * a.nch; }
 
@@ -971,93 +958,103 @@ E0_DEV void fused_lora_item(const DecodeArgs &a, int l) {
 // Slot of routed expert k of layer l (batch 1), or -1 with the reason in
 // `bits` (E0_DEV_BAD_ID / E0_DEV_NOT_RESIDENT). The result is wave-uniform.
 E0_DEV int routed_slot(const DecodeArgs &a, int l, int k, int &bits) {
-    const int e = a.idx[(int64_t)l * a.K + k];
-    int slot = -1;
-    bits = 0;
-    if (e < 0 || e >= a.E) {
-        bits = E0_DEV_BAD_ID;
-    } else {
-        slot = a.slot_of[(int64_t)l * a.E + e];
-        if (slot < 0 || slot >= a.S) {
-            bits = E0_DEV_NOT_RESIDENT;
-            slot = -1;
-        }
-    }
-    return __builtin_amdgcn_readfirstlane(slot);
+    const int e = cload(a.idx, (int64_t)l * a.K + k);
+    const int slot = cload(a.slot_of, (int64_t)l * a.E + min(max(e, 0), a.E - 1));
+    bits = (e < 0 || e >= a.E) ? E0_DEV_BAD_ID : (slot < 0 || slot >= a.S) ? E0_DEV_NOT_RESIDENT : 0;
+    return __builtin_amdgcn_readfirstlane(bits ? -1 : slot);
 }
 
-// Gate/up rows of unit u (SHARED: the shared expert, else routed expert u):
-// hidden units 32c .. 32c + 32, written as the h block (u, c).
+// Gate/up rows of unit u (SHARED: the shared expert, else routed expert u).
+// Item cg covers hidden units 64cg .. 64cg + 64; wavefront w owns half hf =
+// w % 2 of h block c = 2cg + w / 2, i.e. the gate and up rows of 16 hidden
+// units, streamed in 4 batches of 4 units with the loads of the next batch in
+// flight while one is computed. It publishes its half block with its own
+// flag, so the wavefronts of an item never wait on each other.
 template <int NP, bool SHARED>
-E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int c, float *s_small) {
-    constexpr int NB = kFuseCh / (kFuseWaves * kFlatBatch);  // batches of kFlatBatch hidden units per wavefront
+E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *s_small) {
+    constexpr int NBT = 16 / kFlatBatch;  // batches per half block
     const int lane = threadIdx.x & 63, wv = wave_id();
+    const int c = cg * 2 + wv / 2, hf = wv % 2;
     const int d = a.d, ngrp = d / kGroup;
-    const int row0 = c * kFuseCh + wv * (NB * kFlatBatch);
-    float *s_av = s_small;              // [2r] LoRA A x
-    float *s_hv = s_small + 2 * kMaxR;  // [32] h of this item
-    // x of this layer first: it does not depend on the slot.
-    uint32_t xp[NP][4][4];
-    float xs[NP], xc[NP];
+    const int row0 = c * 32 + hf * 16;
+    float *s_av = s_small;                        // [2r] LoRA A x
+    float *s_hv = s_small + 2 * kMaxR + wv * 16;  // this wavefront's 16 h values
+    // Prologue: the kernel arguments in one batch, the slot, the weight loads
+    // of the first two batches, then the loads of x (in-order load counters:
+    // x issued earlier would put its latency in front of the weight loads).
+    const Part *parts = SHARED ? a.sh.p : a.pool.p;
+    const char *base[6];
+    int64_t sstride[6];
 #pragma unroll
-    for (int np = 0; np < NP; ++np) {
-        xs[np] = 0.0f;
-        xc[np] = 0.0f;
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(a.x + (int64_t)l * d + (np * 64 + lane) * 32 + wd * 8);
-            x_pairs_m(v, xp[np][wd], xs[np], xc[np]);
-        }
+    for (int i = 0; i < 6; ++i) {
+        base[i] = parts[i].ptr + (int64_t)l * parts[i].layer_stride;
+        sstride[i] = parts[i].slot_stride;
     }
+    __asm__ __volatile__("" ::"s"(base[0]), "s"(base[1]), "s"(base[2]), "s"(base[3]),
+                         "s"(base[4]), "s"(base[5]), "s"(sstride[0]), "s"(sstride[1]), "s"(sstride[2]),
+                         "s"(sstride[3]), "s"(sstride[4]), "s"(sstride[5]));
     int bits = 0;
     const int slot = SHARED ? 0 : routed_slot(a, l, u, bits);
-    if (bits && c == 0 && threadIdx.x == 0) set_err(a.err, bits);
+    if (bits && cg == 0 && threadIdx.x == 0) set_err(a.err, bits);
     const bool lora = SHARED && a.r > 0;
     if (lora) {
-        // A x of this layer, from its lora item.
+        // A x of this layer, from its lora item (the whole workgroup waits).
         if (!wait_ready(a.flags + l, 1, a.epoch) && threadIdx.x == 0) set_err(a.err, E0_DEV_SYNC_TIMEOUT);
         if (threadIdx.x < 2 * a.r) s_av[threadIdx.x] = coherent_load(a.lora_a + (int64_t)l * 3 * a.r + threadIdx.x);
         __syncthreads();
     }
     if (slot >= 0) {
-        u32x4 q[NB][kFlatBatch][2][NP];
-        // Scales and biases are group-major, so the 8 consecutive rows of this
-        // wavefront and the lane's group are 16 contiguous bytes each.
-        static_assert(NB * kFlatBatch == 8, "one 16-byte scale load covers the wavefront's rows");
-        u32x4 sv[2][NP], bv[2][NP];
+        rsrc_t qr[2], sr[2], br[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const Part pq = SHARED ? a.sh.p[3 * m] : a.pool.p[3 * m];
-            const Part ps = SHARED ? a.sh.p[3 * m + 1] : a.pool.p[3 * m + 1];
-            const Part pb = SHARED ? a.sh.p[3 * m + 2] : a.pool.p[3 * m + 2];
-            const rsrc_t qr = make_rsrc(part_at(pq, l, slot), (uint32_t)a.f * d / 2);
-            const rsrc_t sr = make_rsrc(part_at(ps, l, slot), (uint32_t)a.f * ngrp * 2);
-            const rsrc_t br = make_rsrc(part_at(pb, l, slot), (uint32_t)a.f * ngrp * 2);
+            qr[m] = make_rsrc(base[3 * m] + slot * sstride[3 * m], (uint32_t)a.f * d / 2);
+            sr[m] = make_rsrc(base[3 * m + 1] + slot * sstride[3 * m + 1], (uint32_t)a.f * ngrp * 2);
+            br[m] = make_rsrc(base[3 * m + 2] + slot * sstride[3 * m + 2], (uint32_t)a.f * ngrp * 2);
+        }
+        // One batch: rows r0 .. r0 + 3 of gate and up. Scales and biases are
+        // stored in 8-row tiles, so the lane's 4 rows of one group are 8
+        // contiguous bytes, and the lanes of a load cover whole tiles.
+        struct Stage {
+            u32x4 q[kFlatBatch][2][NP];
+            uint32_t sc[2][NP][2], bi[2][NP][2];
+        };
+        auto load = [&](int bt, Stage &S) {
+            const uint32_t r0 = (uint32_t)(row0 + bt * kFlatBatch);
 #pragma unroll
-            for (int np = 0; np < NP; ++np) {
-                const uint32_t g = (uint32_t)(np * 64 + lane) / 2;
-                sv[m][np] = ld128(sr, (g * (uint32_t)a.f + (uint32_t)row0) * 2);
-                bv[m][np] = ld128(br, (g * (uint32_t)a.f + (uint32_t)row0) * 2);
-            }
+            for (int m = 0; m < 2; ++m) {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
+                for (int np = 0; np < NP; ++np) {
+                    const uint32_t col = (uint32_t)(np * 64 + lane);
 #pragma unroll
-                for (int rr = 0; rr < kFlatBatch; ++rr) {
-                    const uint32_t row = (uint32_t)(row0 + nb * kFlatBatch + rr);
-#pragma unroll
-                    for (int np = 0; np < NP; ++np) {
-                        const uint32_t col = (uint32_t)(np * 64 + lane);
-                        q[nb][rr][m][np] = ld128(qr, row * (d / 2) + col * 16);
-                    }
+                    for (int rr = 0; rr < kFlatBatch; ++rr) S.q[rr][m][np] = ld128(qr[m], (r0 + rr) * (d / 2) + col * 16);
+                    const uint32_t so = sb_index(r0, col / 2, (uint32_t)ngrp) * 2;  // 4 rows inside one 8-row tile
+                    const auto sv = __builtin_amdgcn_raw_buffer_load_b64(sr[m], (int)so, 0, 0);
+                    const auto bv = __builtin_amdgcn_raw_buffer_load_b64(br[m], (int)so, 0, 0);
+                    S.sc[m][np][0] = sv[0];
+                    S.sc[m][np][1] = sv[1];
+                    S.bi[m][np][0] = bv[0];
+                    S.bi[m][np][1] = bv[1];
                 }
             }
-        }
-        // Every load of the item is issued before the first use (keeps the
-        // compiler from spreading them through the compute phase).
-        __asm__ __volatile__("" ::: "memory");
-        const MagicConsts mk = magic_consts();
+        };
+        Stage A, B;
+        load(0, A);
+        load(1, B);
+        u32x4 xr[NP][4];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
+        for (int np = 0; np < NP; ++np)
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd)
+                xr[np][wd] = *reinterpret_cast<const u32x4 *>(a.x + (int64_t)l * d + (np * 64 + lane) * 32 + wd * 8);
+        uint32_t xp[NP][4][4];
+        float xs[NP];
+#pragma unroll
+        for (int np = 0; np < NP; ++np) {
+            xs[np] = 0.0f;
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd) x_pairs_m(xr[np][wd], xp[np][wd], xs[np]);
+        }
+        auto compute = [&](int bt, const Stage &S) {
             float acc[2 * kFlatBatch];
 #pragma unroll
             for (int rr = 0; rr < kFlatBatch; ++rr) {
@@ -1068,11 +1065,10 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int c, float *s
                     for (int np = 0; np < NP; ++np) {
                         float dacc = 0.0f;
 #pragma unroll
-                        for (int wd = 0; wd < 4; ++wd) dacc = dot_word_m(q[nb][rr][m][np][wd], xp[np][wd], dacc, mk);
-                        const int j = nb * kFlatBatch + rr;  // row within the wavefront's 8
-                        const float sc = (float)as_h2(sv[m][np][j / 2])[j % 2];
-                        const float bi = (float)as_h2(bv[m][np][j / 2])[j % 2];
-                        v += sc * dacc + (bi * xs[np] - sc * xc[np]);
+                        for (int wd = 0; wd < 4; ++wd) dacc = dot_word_m(S.q[rr][m][np][wd], xp[np][wd], dacc);
+                        const float sc = (float)as_h2(S.sc[m][np][rr / 2])[rr % 2];
+                        const float bi = (float)as_h2(S.bi[m][np][rr / 2])[rr % 2];
+                        v += (sc * kDenormScale) * dacc + bi * xs[np];
                     }
                     acc[m * kFlatBatch + rr] = v;
                 }
@@ -1082,7 +1078,7 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int c, float *s
             group_reduce_scatter<2 * kFlatBatch, kWave>(acc);
             constexpr int DUP = kWave / (2 * kFlatBatch);
             const int vi = lane / DUP, m = vi / kFlatBatch, rr = vi % kFlatBatch;
-            const int row = row0 + nb * kFlatBatch + rr;
+            const int row = row0 + bt * kFlatBatch + rr;
             float val = acc[0];
             if (lora) {
                 const uint16_t *brow = a.lb[m] + (int64_t)l * (a.lb_ls[m] / 2) + (int64_t)row * a.r;
@@ -1091,19 +1087,35 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int c, float *s
                 val += a.lscale * dl;
             }
             const float other = __shfl_xor(val, 32);
-            if (m == 0 && lane % DUP == 0) s_hv[row - c * kFuseCh] = silu(val) * other;
+            if (m == 0 && lane % DUP == 0) s_hv[bt * kFlatBatch + rr] = silu(val) * other;
+        };
+        // Two-stage pipeline; the empty asm statements keep the compiler from
+        // hoisting later batches' loads (register pressure) or sinking them.
+#pragma unroll
+        for (int bt = 0; bt < NBT; ++bt) {
+            __asm__ __volatile__("" ::: "memory");
+            if (bt & 1) {
+                compute(bt, B);
+                __asm__ __volatile__("" ::: "memory");
+                if (bt + 2 < NBT) load(bt + 2, B);
+            } else {
+                compute(bt, A);
+                __asm__ __volatile__("" ::: "memory");
+                if (bt + 2 < NBT) load(bt + 2, A);
+            }
         }
-    } else if (threadIdx.x < kFuseCh) {
-        s_hv[threadIdx.x] = 0.0f;
+    } else if (lane < 16) {
+        s_hv[lane] = 0.0f;
     }
-    __syncthreads();
-    // The h block of this item (wavefront 0): hi/lo fp16 pairs of h with the
-    // odd pairs scaled by 1/16, the sum and the offset sum.
-    if (threadIdx.x < 64) {
-        const int t = threadIdx.x & 31;
+    wave_lds_sync();
+    // This wavefront's half of the h block: hi/lo fp16 pairs of h with the
+    // odd pairs scaled by 1/16 (the form dot_word_m2 takes), and the half's sum.
+    {
+        const int t = lane & 15;
         const float v = s_hv[t];
-        if (lora && threadIdx.x < kFuseCh) coherent_store(hrow(a, l, u) + c * kFuseCh + t, v);
-        const int p = t % 8, j = p % 4;
+        if (lora && lane < 16) coherent_store(hrow(a, l, u) + row0 + t, v);
+        const int tb = hf * 16 + t;  // element of the block
+        const int p = tb % 8, j = p % 4;
         const float hv = (j & 1) ? v * 0.0625f : v;
         const f16 hi = (f16)hv;
         const f16 lo = (f16)(hv - (float)hi);
@@ -1112,22 +1124,23 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int c, float *s
         const uint32_t hpart = __shfl_xor((int)hbits, 4), lpart = __shfl_xor((int)lbits, 4);
         float se = (j & 1) ? 0.0f : v, so = (j & 1) ? v : 0.0f;
 #pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) {
+        for (int o = 8; o >= 1; o >>= 1) {
             se += __shfl_xor(se, o);
             so += __shfl_xor(so, o);
         }
         uint32_t *blk = hblk(a, l, u, c);
-        if (threadIdx.x < 32 && p < 4) {
-            const int dw = (t / 8) * 4 + j;
+        if (lane < 16 && p < 4) {
+            const int dw = (tb / 8) * 4 + j;
             __hip_atomic_store(blk + dw, hbits | (hpart << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(blk + 16 + dw, lbits | (lpart << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (threadIdx.x == 0) {
-            coherent_store(reinterpret_cast<float *>(blk + kBlkSum), se + so);
-            coherent_store(reinterpret_cast<float *>(blk + kBlkCorr), 1024.0f * se + 64.0f * so);
-        }
+        if (lane == 0) coherent_store(reinterpret_cast<float *>(blk + kBlkSum + 2 * hf), se + so);
     }
-    signal_ready(gu_flags(a, l) + (int64_t)u * a.nch + c, a.epoch);
+    // This wavefront's stores complete, then its flag.
+    __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");
+    if (lane == 0)
+        __hip_atomic_store(gu_flags(a, l) + (int64_t)u * a.nch + 2 * c + hf, a.epoch, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Down rows: LPR lanes per row (d_ff = 32 * LPR), KM routed units at most
@@ -1143,25 +1156,29 @@ E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, 
     const int K = a.K;
     const int row0 = rb * (kFuseWaves * RW) + wv * RW;
 
-    // 1. Slots of every routed unit (all scalar loads issued together), then
-    //    every weight load, before the wait.
+    // 1. Slots of every routed unit, then every weight load, before the wait.
+    //    The id, weight and slot-table reads are unconditional (indices
+    //    clamped into range, invalid results masked afterwards), so they go
+    //    out as two batches of scalar loads rather than one at a time.
     int e[KM], slot[KM];
     float wk[KM];
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
-        e[k] = k < K ? a.idx[(int64_t)l * K + k] : -1;
-        wk[k] = k < K ? a.w[(int64_t)l * K + k] : 0.0f;
+        const int kk = k < K ? k : K - 1;
+        e[k] = cload(a.idx, (int64_t)l * K + kk);
+        wk[k] = k < K ? cload(a.w, (int64_t)l * K + kk) : 0.0f;
     }
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
-        slot[k] = (e[k] >= 0 && e[k] < a.E) ? a.slot_of[(int64_t)l * a.E + e[k]] : -1;
-        if (slot[k] >= a.S) slot[k] = -1;
+        const bool ok = k < K && e[k] >= 0 && e[k] < a.E;
+        const int sl = cload(a.slot_of, (int64_t)l * a.E + min(max(e[k], 0), a.E - 1));
+        slot[k] = __builtin_amdgcn_readfirstlane((ok && sl >= 0 && sl < a.S) ? sl : -1);
     }
     // Loads are issued without branches (a branch around a load makes the
     // compiler wait for it at the join): a unit that does not exist or has
     // no valid slot reads through a zero-size buffer descriptor, which returns
     // zeros without touching memory, and contributes nothing. Lane group grp
-    // owns IT consecutive rows, so its group-major scales (and biases) are
+    // owns IT consecutive rows inside one 8-row tile, so its scales (and biases) are
     // 2 * IT contiguous bytes.
     static_assert(IT == 2 || IT == 4 || IT == 8, "scale loads of 4, 8 or 16 bytes");
     u32x4 q[KM + 1][IT];
@@ -1187,7 +1204,7 @@ E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, 
         const rsrc_t bb = make_rsrc(part_at(pb, l, s0), on ? (uint32_t)d * fgrp * 2 : 0u);
 #pragma unroll
         for (int it = 0; it < IT; ++it) q[u][it] = ld128(qb, (uint32_t)(rows0 + it) * (f / 2) + gl * 16);
-        const uint32_t so = ((uint32_t)(gl / 2) * d + (uint32_t)rows0) * 2;
+        const uint32_t so = sb_index((uint32_t)rows0, (uint32_t)(gl / 2), (uint32_t)fgrp) * 2;  // IT rows in one tile
         load_halves(sb, so, sv[u]);
         load_halves(bb, so, bv[u]);
     };
@@ -1232,7 +1249,6 @@ E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, 
         __syncthreads();
     }
     // 3. y rows: routed units in k order, then the shared expert (weight 1).
-    const MagicConsts mk = magic_consts();
     float acc[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) acc[it] = 0.0f;
@@ -1249,15 +1265,14 @@ E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, 
                 hlo[4 * i + j] = w2[j];
             }
         }
-        const float hsum = __builtin_bit_cast(float, blk[kBlkSum]);
-        const float hcorr = __builtin_bit_cast(float, blk[kBlkCorr]);
+        const float hsum = __builtin_bit_cast(float, blk[kBlkSum]) + __builtin_bit_cast(float, blk[kBlkSum + 2]);
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             float dacc = 0.0f;
 #pragma unroll
-            for (int wd = 0; wd < 4; ++wd) dacc = dot_word_m2(q[u][it][wd], hh + 4 * wd, hlo + 4 * wd, dacc, mk);
+            for (int wd = 0; wd < 4; ++wd) dacc = dot_word_m2(q[u][it][wd], hh + 4 * wd, hlo + 4 * wd, dacc);
             const float sc = (float)as_h2(sv[u][it / 2])[it % 2], bi = (float)as_h2(bv[u][it / 2])[it % 2];
-            acc[it] += wk * (sc * dacc + (bi * hsum - sc * hcorr));
+            acc[it] += wk * ((sc * kDenormScale) * dacc + bi * hsum);
         }
     };
 #pragma unroll
@@ -1282,22 +1297,45 @@ template <int NP, int LPR, int KM, int RW>
 __global__ __launch_bounds__(kFuseThreads) void decode_fused_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t s_hb[(KM + 1) * LPR * kBlk];
     __shared__ float s_hsh[32 * LPR];
-    __shared__ float s_small[2 * kMaxR + kFuseCh];
-    const int item = blockIdx.x;
+    __shared__ float s_small[2 * kMaxR + kFuseWaves * 16];
+    // Item order: the lora items, then steps s = 0 .. L + lag - 1, step s
+    // holding the gate/up items of layer s (s < L) followed by the down items
+    // of layer s - lag (s >= lag). Every down item comes after all gate/up
+    // items of its layer, and by the time it is dispatched they have had
+    // about a machine's worth of other items to finish in.
+    int item = blockIdx.x;
     if (item < a.n_lora) {
         fused_lora_item(a, item);
-    } else if (item < a.n_lora + a.n_gu) {
-        const int t = item - a.n_lora;
-        const int per_l = a.units * a.nch;
-        const int l = t / per_l, u = (t % per_l) / a.nch, c = t % a.nch;
-        if (u < a.K)
-            fused_gateup_item<NP, false>(a, l, u, c, s_small);
-        else
-            fused_gateup_item<NP, true>(a, l, u, c, s_small);
+        return;
+    }
+    item -= a.n_lora;
+    const int n1 = a.n_gu, n2 = a.n_dn, lag = a.lag, L = a.L;
+    int l, r, gu;
+    if (item < lag * n1) {
+        gu = 1;
+        l = item / n1;
+        r = item % n1;
+    } else if ((item -= lag * n1) < (L - lag) * (n1 + n2)) {
+        const int st = item / (n1 + n2);
+        r = item % (n1 + n2);
+        gu = r < n1;
+        l = gu ? lag + st : st;
+        if (!gu) r -= n1;
     } else {
-        const int t = item - a.n_lora - a.n_gu;
-        const int per_l = a.d / (kFuseWaves * RW);
-        fused_down_item<LPR, KM, RW>(a, t / per_l, t % per_l, s_hb, s_hsh, s_small);
+        item -= (L - lag) * (n1 + n2);
+        gu = 0;
+        l = L - lag + item / n2;
+        r = item % n2;
+    }
+    if (gu) {
+        const int per_u = a.nch / kFuseWaves;  // items per unit
+        const int u = r / per_u, cg = r % per_u;
+        if (u < a.K)
+            fused_gateup_item<NP, false>(a, l, u, cg, s_small);
+        else
+            fused_gateup_item<NP, true>(a, l, u, cg, s_small);
+    } else {
+        fused_down_item<LPR, KM, RW>(a, l, r, s_hb, s_hsh, s_small);
     }
 }
 
@@ -1345,7 +1383,7 @@ Layout decode_layout(int L, int B, int K, int E, int f, int r) {
     o.lora = off;
     off = e0_align(off + sizeof(float) * (size_t)L * B * 3 * (r > 0 ? r : 1));
     o.flags = off;
-    off = e0_align(off + (B == 1 ? sizeof(uint64_t) * (size_t)L * (1 + (K + 1) * (size_t)(f / kFuseCh)) : 0));
+    off = e0_align(off + (B == 1 ? sizeof(uint64_t) * (size_t)L * (1 + (K + 1) * (size_t)(f / kHalfBlk)) : 0));
     o.hblk = off;
     off = e0_align(off + (B == 1 ? sizeof(uint32_t) * (size_t)L * (K + 1) * (size_t)(f / 32) * kBlk : 0));
     o.total = off;
@@ -1482,20 +1520,29 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
     hipStream_t st = static_cast<hipStream_t>(stream);
     e0_status s;
     const int U = K + (a.has_shared ? 1 : 0);
-    if (B == 1 && lpr_d == 64 && np == 1 && (lpr_f == 8 || lpr_f == 16 || (lpr_f == 32 && K <= 4)) && K <= 8) {
+    if (B == 1 && lpr_d == 64 && np == 1 && (lpr_f == 8 || lpr_f == 16 || (lpr_f == 32 && K <= 4)) && K <= 8 &&
+        f % (kHalfBlk * kFuseWaves) == 0) {
         // Batch 1, d_model 2048: the single-launch kernel.
         a.epoch = e0_next_epoch();
         a.units = U;
-        a.nch = f / kFuseCh;
+        a.nch = f / kHalfBlk;
         a.n_lora = (a.has_shared && r > 0) ? L : 0;
         const bool small = K <= 4;
         // output rows per wavefront of a down item (at least two load
         // instructions per unit, so its scales are one 4/8/16-byte load)
         const int rw = (small || lpr_f == 8) ? 16 : 8;
-        const int64_t n_gu = (int64_t)L * U * a.nch, n_dn = (int64_t)L * (d / (kFuseWaves * rw));
-        E0_REQUIRE(a.n_lora + n_gu + n_dn <= (int64_t)INT32_MAX, E0_ERR_CAPACITY);
+        const int64_t n_gu = (int64_t)U * (a.nch / kFuseWaves), n_dn = d / (kFuseWaves * rw);  // per layer
+        E0_REQUIRE(a.n_lora + L * (n_gu + n_dn) <= (int64_t)INT32_MAX, E0_ERR_CAPACITY);
         a.n_gu = (int)n_gu;
-        const dim3 grid((unsigned)(a.n_lora + n_gu + n_dn));
+        a.n_dn = (int)n_dn;
+        // Lag of the down items: about one machine's worth of resident
+        // workgroups (three per compute unit) between a layer's gate/up items
+        // and its down items.
+        static int cus = 0;
+        if (!cus && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess) cus = 256;
+        const int64_t lag = (3 * (int64_t)cus + n_gu + n_dn - 1) / (n_gu + n_dn) + 1;
+        a.lag = (int)(lag < L ? lag : L);
+        const dim3 grid((unsigned)(a.n_lora + L * (n_gu + n_dn)));
         switch (lpr_f) {
             case 8:
                 if (small) hipLaunchKernelGGL((decode_fused_kernel<1, 8, 4, 16>), grid, dim3(kFuseThreads), 0, st, a);

@@ -48,6 +48,10 @@ E0_DEV const char *part_at(const Part &p, int layer, int slot) {
 
 E0_DEV float h2f(uint16_t b) { return (float)__builtin_bit_cast(f16, b); }
 
+// Element index of the scale (or bias) of row r, group g in the bundle's
+// 8-row tiles [rows/8][ngrp][8].
+E0_DEV uint32_t sb_index(uint32_t r, uint32_t g, uint32_t ngrp) { return ((r >> 3) * ngrp + g) * 8 + (r & 7); }
+
 // Reinterpret a dword as two fp16. Takes the dword by value: applying
 // __builtin_bit_cast directly to an element of an ext_vector (v[j]) reads the
 // vector's first element whatever j is, so every such cast goes through here.
@@ -62,6 +66,16 @@ E0_DEV rsrc_t make_rsrc(const void *p, uint32_t bytes) {
 }
 E0_DEV u32x4 ld128(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0); }
 E0_DEV uint16_t ld16(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0); }
+
+// A read through the constant address space: with a wave-uniform index it
+// becomes a scalar load (several issued together, one wait), for small tables
+// that no kernel writes while the reading kernel runs (routing ids and
+// weights, slot tables).
+template <class T>
+E0_DEV T cload(const T *p, int64_t i) {
+    typedef const __attribute__((address_space(4))) T ct;
+    return ((ct *)p)[i];
+}
 
 E0_DEV float wave_sum(float v) {
 #pragma unroll

@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kGemmThreads) void prefill_gemm_kernel(PrefillArgs 
 #pragma unroll
         for (int mt = 0; mt < NM; ++mt) {
             q[mt] = ld128(qr[mt], (uint32_t)col * (Kdim / 2) + g * 32 + h * 16);
-            const uint32_t so = ((uint32_t)g * Nall + col) * 2;  // group-major scales
+            const uint32_t so = sb_index((uint32_t)col, (uint32_t)g, (uint32_t)ngroups) * 2;
             sb[mt] = (uint32_t)ld16(sr[mt], so) | ((uint32_t)ld16(br[mt], so) << 16);
         }
     };
