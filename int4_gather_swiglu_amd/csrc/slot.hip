@@ -15,7 +15,9 @@
 // from the candidates.
 //
 // Two launches: plan (one workgroup per layer: sets, compaction, tables, copy
-// list) and copy (many workgroups: 16-byte vector copies of the nine parts).
+// list) and copy (many workgroups: 16-byte vector copies of the nine parts,
+// one linear range per expert when store and pool hold whole bundles, with
+// streaming loads and stores so the copy does not evict cached weights).
 #include "e0_internal.h"
 
 namespace {
@@ -139,15 +141,33 @@ struct CopyArgs {
     Stack store, pool;
     int64_t part_units[9];  // 16-byte units per part
     int64_t part_end[9];    // cumulative units
+    int contiguous;         // store and pool are bundle-contiguous
 };
 
 __global__ __launch_bounds__(kThreads) void slot_copy_kernel(CopyArgs a) {
     const int l = blockIdx.x, i = blockIdx.y;
-    if (i >= a.ncopy[l]) return;
-    const int slot = a.copy_slot[(int64_t)l * a.maxc + i];
-    const int e = a.copy_exp[(int64_t)l * a.maxc + i];
+    if (i >= cload(a.ncopy, l)) return;
+    const int slot = cload(a.copy_slot, (int64_t)l * a.maxc + i);
+    const int e = cload(a.copy_exp, (int64_t)l * a.maxc + i);
     const int64_t u0 = (int64_t)blockIdx.z * (kCopyChunk / 16);
     u32x4 v[kCopyUnits];
+    if (a.contiguous) {
+        // Store and pool hold whole bundles: one linear range per expert.
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(part_at(a.store.p[0], l, e));
+        u32x4 *dst = reinterpret_cast<u32x4 *>(const_cast<char *>(part_at(a.pool.p[0], l, slot)));
+        const int64_t n = a.part_end[8];
+#pragma unroll
+        for (int k = 0; k < kCopyUnits; ++k) {
+            const int64_t u = u0 + (int64_t)k * kThreads + threadIdx.x;
+            if (u < n) v[k] = __builtin_nontemporal_load(src + u);
+        }
+#pragma unroll
+        for (int k = 0; k < kCopyUnits; ++k) {
+            const int64_t u = u0 + (int64_t)k * kThreads + threadIdx.x;
+            if (u < n) __builtin_nontemporal_store(v[k], dst + u);
+        }
+        return;
+    }
     int64_t dst_off[kCopyUnits];
     int dst_part[kCopyUnits];
 #pragma unroll
@@ -167,8 +187,19 @@ __global__ __launch_bounds__(kThreads) void slot_copy_kernel(CopyArgs a) {
     for (int k = 0; k < kCopyUnits; ++k) {
         if (dst_part[k] < 0) continue;
         u32x4 *dst = reinterpret_cast<u32x4 *>(const_cast<char *>(part_at(a.pool.p[dst_part[k]], l, slot))) + dst_off[k];
-        *dst = v[k];
+        __builtin_nontemporal_store(v[k], dst);
     }
+}
+
+// True when every part of the stack sits at its bundle offset from part 0
+// with part 0's strides (bundle-contiguous storage).
+bool stack_contiguous(const e0_stack *s, const int64_t (&part_end)[9]) {
+    for (int j = 1; j < 9; ++j) {
+        const e0_part &p = s->part[j], &p0 = s->part[0];
+        if (static_cast<const char *>(p.ptr) != static_cast<const char *>(p0.ptr) + part_end[j - 1] * 16) return false;
+        if (p.slot_stride != p0.slot_stride || p.layer_stride != p0.layer_stride) return false;
+    }
+    return true;
 }
 
 bool stack_ok(const e0_stack *s) {
@@ -250,6 +281,7 @@ extern "C" e0_status e0_slot_update(const e0_moe_dims *dims, int32_t L, int32_t 
     c.copy_exp = a.copy_exp;
     c.store = to_stack(*store);
     c.pool = to_stack(*pool);
+    c.contiguous = stack_contiguous(store, c.part_end) && stack_contiguous(pool, c.part_end);
     hipLaunchKernelGGL(slot_copy_kernel, dim3(L, lay.maxc, (unsigned)chunks), dim3(kThreads), 0, st, c);
     return e0_launch_status();
 }
