@@ -11,21 +11,19 @@
 //
 // Launches (one stream):
 //  1. sort     (1 workgroup): counting sort of the T*K pairs by expert (LDS
-//               counters, one scan, scatter), the row offset of every
-//               expert and the list of 128-row M-tiles.
+//               counters, one scan, scatter of the pair index and its routing
+//               weight), the row offset of every expert and the list of
+//               128-row M-tiles.
 //  2. gemm1    (tiles x d_ff/128): H = silu(X G^T) * (X U^T) for one M-tile
 //               and 128 columns of d_ff, X gathered through the sort; H fp16.
-//  3. gemm2    (tiles x d_model/128): Yb[pair] = w_pair * (H D^T).
+//  3. gemm2    (tiles x d_model/256): Yb[pair] = w_pair * (H D^T).
 //  4. combine  : y[t] = sum over k in order of Yb[t*K + k].
+// The last M-tile of an expert runs only the 32-row MFMA blocks that hold
+// rows. Work items are dealt to the eight XCDs in contiguous ranges.
 //
-// MFMA v_mfma_f32_32x32x16_f16. Inside each 64-wide quantisation group the
-// reduction index is permuted the same way on both operands (so the sum is
-// unchanged): lane half h of MFMA j covers inputs 32h + 8j .. 32h + 8j + 7, in
-// the order (0,4,1,5,2,6,3,7). A lane's B fragment for the four MFMAs of a
-// group is then one 16-byte load of four code words of its column, and each
-// word dequantises as four (q_c, q_{c+4}) pairs: 1024+q by bit placement,
-// minus 1024 exactly, then one fp16 fma s*q + b (a single rounding of the
-// exact dequantised weight).
+// MFMA v_mfma_f32_32x32x16_f16 on fp16 operands. A rows go from global memory
+// straight into LDS; B fragments are code words dequantised in registers (one
+// fp16 fma per weight, a single rounding of the exact dequantised value).
 #include "e0_internal.h"
 
 #include <math.h>
@@ -33,11 +31,11 @@
 namespace {
 
 constexpr int kTM = 128;         // rows per M-tile
-constexpr int kTN = 128;         // columns per workgroup (4 waves x 32)
 constexpr int kGemmThreads = 256;
 constexpr int kSortThreads = 1024;
 constexpr int kMaxSortE = 1024;
-constexpr int kARowPad = 72;     // halves per LDS row of A (64 + 8 padding)
+constexpr int kStepK = 128;      // reduction inputs per pipeline step (two groups)
+constexpr int kARow = kStepK;    // halves per LDS row of A (XOR-swizzled chunks, no padding)
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
@@ -52,6 +50,7 @@ struct PrefillArgs {
     int32_t *err;
     int32_t *off;       // [E + 1] first sorted row of each expert
     int32_t *perm;      // [n] pair index at each sorted row
+    float *wsort;       // [n] routing weight of the pair at each sorted row
     int32_t *ntiles;    // [1]
     int32_t *tile_e;    // [max_tiles]
     int32_t *tile_m0;   // [max_tiles]
@@ -130,7 +129,12 @@ __global__ __launch_bounds__(kSortThreads) void prefill_sort_kernel(PrefillArgs 
     // GEMM row is computed on its own and results are stored by pair index).
     for (int p = tid; p < n; p += kSortThreads) {
         const int e = a.idx[p];
-        if (e >= 0 && e < E) a.perm[atomicAdd(&s_fill[e], 1)] = p;
+        const float wp = a.w[p];
+        if (e >= 0 && e < E) {
+            const int row = atomicAdd(&s_fill[e], 1);
+            a.perm[row] = p;
+            a.wsort[row] = wp;
+        }
     }
 }
 
@@ -143,154 +147,258 @@ E0_DEV uint32_t and_or_v(uint32_t x, uint32_t m, uint32_t c) {
     return r;
 }
 
-// Eight fp16 weights of one code word, in the pair order (q0,q4,q1,q5,...):
-// s * q + b with one rounding. s2 / b2 hold (s, s) / (b, b).
-E0_DEV h8 dequant_word(uint32_t w, f16x2 s2, f16x2 b2, uint32_t m, uint32_t c) {
-    const f16x2 k1024 = f16x2{(f16)1024.0f, (f16)1024.0f};
-    h8 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const f16x2 t = as_h2(and_or_v(w >> (4 * j), m, c)) - k1024;  // (q_j, q_{j+4}), exact
-        const f16x2 v = __builtin_elementwise_fma(t, s2, b2);
-        o[2 * j] = v[0];
-        o[2 * j + 1] = v[1];
-    }
-    return o;
+// Weights 2p and 2p + 1 of one code word: s * q + b with one rounding each.
+// Byte p holds (q_2p, q_2p+1); placing it in both halves and masking gives
+// (1024 + q_2p, 1024 + 16 q_2p+1) by bit placement, and one fma with
+// (1, 1/16) and (-1024, -64) turns that into (q_2p, q_2p+1) exactly.
+E0_DEV f16x2 dequant_pair(uint32_t w, int p, f16x2 s2, f16x2 b2, uint32_t m, uint32_t c) {
+    const f16x2 kmul = f16x2{(f16)1.0f, (f16)0.0625f};
+    const f16x2 kadd = f16x2{(f16)-1024.0f, (f16)-64.0f};
+    const uint32_t dup = __builtin_amdgcn_perm(w, w, 0x0c000c00u | (uint32_t)p << 16 | (uint32_t)p);
+    const f16x2 q = __builtin_elementwise_fma(as_h2(and_or_v(dup, m, c)), kmul, kadd);
+    return __builtin_elementwise_fma(q, s2, b2);
 }
 
-// (h0..h7) -> (h0,h4,h1,h5,h2,h6,h3,h7)
-E0_DEV u32x4 permute8(u32x4 v) {
-    u32x4 o;
-    o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
-    o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
-    o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
-    o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
-    return o;
-}
-
-template <bool GATEUP>
-__global__ __launch_bounds__(kGemmThreads) void prefill_gemm_kernel(PrefillArgs a) {
-    constexpr int NM = GATEUP ? 2 : 1;  // matrices: gate and up, or down
-    __shared__ __attribute__((aligned(16))) uint16_t s_a[2][kTM * kARowPad];
-    const int Nall = GATEUP ? a.f : a.d;       // output columns
-    const int Kdim = GATEUP ? a.d : a.f;       // reduction length
+// One 128-row M-tile (rows m0 .. of expert e) times 32 * NB * 4 output
+// columns, of which the first NMB 32-row blocks are computed. GATEUP: the two
+// B operands of a wave are the gate and the up column of one d_ff index, and
+// the epilogue stores H = silu(gate) * up. Down (NB 1 or 2): the B operands
+// are NB adjacent 32-column blocks of d_model, and the epilogue stores the
+// weighted row w_pair * (H D^T).
+//
+// Pipeline step = 128 inputs = two quantisation groups. Lane half h owns
+// group 2s + h of step s whole: its eight code words (32 contiguous bytes of
+// its column) and one scale/bias pair; MFMA j takes word j of each half, so
+// its 16-wide reduction slice is inputs 8j..8j+7 of both groups.
+//
+// A rows go from global memory straight into LDS (global_load_lds_dwordx4:
+// lane L of a wave's load lands at the wave's LDS base + 16 L), so a load
+// covers four rows of 16 chunks; a lane fetches chunk c' ^ (row % 16) for LDS
+// slot c', which makes the fragment reads (32 rows, one chunk) conflict-free.
+// The rows and weights of step s + 1 are requested before the MFMAs of step
+// s and waited for after them. Inside a step, word j + 1 is dequantised and
+// its A fragments read in slices between the MFMAs of word j.
+template <int NB, bool GATEUP, int NMB>
+E0_DEV void prefill_tile(const PrefillArgs &a, uint16_t (*s_a)[kTM * kARow], int e, int m0, int m_end, int nt) {
+    constexpr int kCols = 4 * 32 * (GATEUP ? 1 : NB);  // output columns per workgroup
+    constexpr int kMf = NMB * NB;                      // MFMAs per code word
+    constexpr int kPairs = 4 * NB;                     // weight pairs per code word set
+    constexpr int kPpm = kPairs / kMf > 0 ? kPairs / kMf : 1;  // pairs dequantised per MFMA
+    const int Nall = GATEUP ? a.f : a.d;
+    const int Kdim = GATEUP ? a.d : a.f;
     const int ngroups = Kdim / kGroup;
-    const int nN = Nall / kTN;
-    const int tile = blockIdx.x / nN, nt = blockIdx.x % nN;
-    if (tile >= a.ntiles[0]) return;
-    const int e = a.tile_e[tile], m0 = a.tile_m0[tile];
-    const int m_end = a.off[e + 1];
+    const int nsteps = Kdim / kStepK;
     const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
     const int h = lane >> 5;
-    const int col = nt * kTN + wv * 32 + (lane & 31);  // this lane's output column
 
-    // A staging: chunk c = tid + 256 i covers row c / 8, 8-half block c % 8.
-    const uint16_t *arow[4];
+    // A staging: wave wv loads rows 32 wv .. 32 wv + 31 (only waves below NMB),
+    // load i covering rows 32 wv + 4 i + lane / 16.
+    const int lrow = lane >> 4, lslot = lane & 15;
+    const uint16_t *abase = GATEUP ? a.x : a.H;
+    const int64_t alen = GATEUP ? a.d : a.f;
+    int arow[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = (tid + 256 * i) >> 3;
-        int m = m0 + r;
+    for (int i = 0; i < 8; ++i) {
+        int m = m0 + wv * 32 + 4 * i + lrow;
         if (m >= m_end) m = m0;  // padding rows repeat a valid row; never stored
-        if (GATEUP)
-            arow[i] = a.x + (int64_t)(a.perm[m] / a.K) * a.d;
-        else
-            arow[i] = a.H + (int64_t)m * a.f;
+        arow[i] = GATEUP ? a.perm[m] / a.K : m;
     }
-    const int akb = tid & 7;
-    auto stage = [&](int g, int buf) {
-        u32x4 v[4];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)&s_a[0][0];
+    auto load_a = [&](int st, int buf) {
+        if (wv >= NMB) return;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4 *>(arow[i] + g * kGroup + akb * 8);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = (tid + 256 * i) >> 3;
-            *reinterpret_cast<u32x4 *>(&s_a[buf][r * kARowPad + akb * 8]) = permute8(v[i]);
+        for (int i = 0; i < 8; ++i) {
+            const int r = wv * 32 + 4 * i + lrow;
+            const int c = lslot ^ (r & 15);
+            const uint16_t *src = abase + arow[i] * alen + st * kStepK + c * 8;
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(buf * kTM * kARow + (wv * 32 + 4 * i) * kStepK) * 2);
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "memory", "m0");
         }
     };
 
-    // B: this lane's column of each matrix.
-    rsrc_t qr[NM], sr[NM], br[NM];
-#pragma unroll
-    for (int mt = 0; mt < NM; ++mt) {
-        const int mi = GATEUP ? mt : 2;
-        qr[mt] = make_rsrc(part_at(a.layer.p[3 * mi + 0], 0, e), (uint32_t)Nall * Kdim / 2);
-        sr[mt] = make_rsrc(part_at(a.layer.p[3 * mi + 1], 0, e), (uint32_t)Nall * ngroups * 2);
-        br[mt] = make_rsrc(part_at(a.layer.p[3 * mi + 2], 0, e), (uint32_t)Nall * ngroups * 2);
+    // Down: pair index and weight of row tid (tid < 128), loaded now and
+    // parked in LDS after the main loop for the epilogue.
+    int my_p = 0;
+    float my_w = 0.0f;
+    if (!GATEUP && tid < kTM && m0 + tid < m_end) {
+        my_p = a.perm[m0 + tid];
+        my_w = a.wsort[m0 + tid];
     }
+
+    // B operands: part base of each and this lane's column.
+    rsrc_t qr[NB], sr[NB], br[NB];
+    uint32_t colb[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+        const int mi = GATEUP ? n : 2;
+        qr[n] = make_rsrc(part_at(a.layer.p[3 * mi + 0], 0, e), (uint32_t)Nall * Kdim / 2);
+        sr[n] = make_rsrc(part_at(a.layer.p[3 * mi + 1], 0, e), (uint32_t)Nall * ngroups * 2);
+        br[n] = make_rsrc(part_at(a.layer.p[3 * mi + 2], 0, e), (uint32_t)Nall * ngroups * 2);
+        colb[n] = GATEUP ? nt * kCols + wv * 32 + (lane & 31) : nt * kCols + wv * 32 * NB + n * 32 + (lane & 31);
+    }
+    // Scale and bias stay apart until their use: packing them right after
+    // the loads would wait for those loads, and with them for every load
+    // issued before.
+    struct Bst {
+        u32x4 q[NB][2];
+        uint32_t s[NB], b[NB];
+    };
+    auto fetch_b = [&](int st, Bst &b) {
+        const int g = 2 * st + h;
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+            const uint32_t qo = colb[n] * (uint32_t)(Kdim / 2) + g * 32;
+            b.q[n][0] = ld128(qr[n], qo);
+            b.q[n][1] = ld128(qr[n], qo + 16);
+            const uint32_t so = sb_index(colb[n], (uint32_t)g, (uint32_t)ngroups) * 2;
+            b.s[n] = ld16(sr[n], so);
+            b.b[n] = ld16(br[n], so);
+        }
+    };
     uint32_t km, kc;
-    __asm__("v_mov_b32 %0, 0x000f000f" : "=v"(km));
+    __asm__("v_mov_b32 %0, 0x00f0000f" : "=v"(km));
     __asm__("v_mov_b32 %0, 0x64006400" : "=v"(kc));
 
-    f16v acc[NM][4];
+    f16v acc[NB][NMB];
 #pragma unroll
-    for (int mt = 0; mt < NM; ++mt)
+    for (int n = 0; n < NB; ++n)
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[mt][mb][v] = 0.0f;
+            for (int v = 0; v < 16; ++v) acc[n][mb][v] = 0.0f;
 
-    // Weight fragments of group g: one 16-byte code load and one scale/bias
-    // pair per matrix; fetched one group ahead of their use.
-    u32x4 qv[NM], qn[NM];
-    uint32_t sbv[NM], sbn[NM];
-    auto fetch_b = [&](int g, u32x4 (&q)[NM], uint32_t (&sb)[NM]) {
+    // Fragment of rows mb*32 .. +31, chunk h*8 + j (inputs h*64 + 8j ..).
+    auto afrag = [&](int buf, int mb, int j) {
+        const int r = mb * 32 + (lane & 31);
+        const int c = (h * 8 + j) ^ (r & 15);
+        return *reinterpret_cast<const h8 *>(&s_a[buf][r * kStepK + c * 8]);
+    };
+    // Pair p (0 .. 4 NB - 1) of code word j: operand p / 4, byte p % 4.
+    auto dq_pair = [&](const Bst &b, int j, int p) {
+        const int n = p >> 2;
+        const f16 sv = __builtin_bit_cast(f16, (uint16_t)b.s[n]), bv = __builtin_bit_cast(f16, (uint16_t)b.b[n]);
+        return dequant_pair(b.q[n][j >> 2][j & 3], p & 3, f16x2{sv, sv}, f16x2{bv, bv}, km, kc);
+    };
+    auto compute = [&](int buf, const Bst &b) {
+        h8 bcur[NB], af[NMB];
 #pragma unroll
-        for (int mt = 0; mt < NM; ++mt) {
-            q[mt] = ld128(qr[mt], (uint32_t)col * (Kdim / 2) + g * 32 + h * 16);
-            const uint32_t so = sb_index((uint32_t)col, (uint32_t)g, (uint32_t)ngroups) * 2;
-            sb[mt] = (uint32_t)ld16(sr[mt], so) | ((uint32_t)ld16(br[mt], so) << 16);
+        for (int p = 0; p < kPairs; ++p) {
+            const f16x2 v = dq_pair(b, 0, p);
+            bcur[p >> 2][2 * (p & 3)] = v[0];
+            bcur[p >> 2][2 * (p & 3) + 1] = v[1];
+        }
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) af[mb] = afrag(buf, mb, 0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            h8 bnx[NB], afn[NMB];
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+                for (int n = 0; n < NB; ++n) {
+                    acc[n][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mb], bcur[n], acc[n][mb], 0, 0, 0);
+                    if (j < 7) {
+                        const int k = mb * NB + n;
+#pragma unroll
+                        for (int q = 0; q < kPpm; ++q) {
+                            const int p = k * kPpm + q;
+                            if (p < kPairs) {
+                                const f16x2 v = dq_pair(b, j + 1, p);
+                                bnx[p >> 2][2 * (p & 3)] = v[0];
+                                bnx[p >> 2][2 * (p & 3) + 1] = v[1];
+                            }
+                        }
+                        if (n == 0) afn[mb] = afrag(buf, mb, j + 1);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if (j < 7) {
+#pragma unroll
+                for (int n = 0; n < NB; ++n) bcur[n] = bnx[n];
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb) af[mb] = afn[mb];
+            }
         }
     };
-    fetch_b(0, qv, sbv);
-    stage(0, 0);
+
+    // Step st: request the rows (into LDS buffer (st + 1) & 1) and weights of
+    // step st + 1, run the MFMAs of step st from buffer st & 1, then wait for
+    // all of them before the barrier.
+    Bst cur, next;
+    fetch_b(0, cur);
+    load_a(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int g = 0; g < ngroups; ++g) {
-        const int buf = g & 1;
-        if (g + 1 < ngroups) {
-            fetch_b(g + 1, qn, sbn);
-            stage(g + 1, buf ^ 1);
+    for (int st = 0; st < nsteps; ++st) {
+        const bool more = st + 1 < nsteps;
+        if (more) {
+            load_a(st + 1, (st + 1) & 1);
+            fetch_b(st + 1, next);
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            h8 bfrag[NM];
-#pragma unroll
-            for (int mt = 0; mt < NM; ++mt) {
-                const f16x2 sb = as_h2(sbv[mt]);
-                bfrag[mt] = dequant_word(qv[mt][j], f16x2{sb[0], sb[0]}, f16x2{sb[1], sb[1]}, km, kc);
-            }
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                const h8 afrag = *reinterpret_cast<const h8 *>(&s_a[buf][(mb * 32 + (lane & 31)) * kARowPad + (h * 4 + j) * 8]);
-#pragma unroll
-                for (int mt = 0; mt < NM; ++mt)
-                    acc[mt][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag, bfrag[mt], acc[mt][mb], 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int mt = 0; mt < NM; ++mt) {
-            qv[mt] = qn[mt];
-            sbv[mt] = sbn[mt];
-        }
+        compute(st & 1, cur);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (more) cur = next;
         __syncthreads();
     }
 
     // Epilogue. C layout: lane, v -> row 8 (v / 4) + 4 h + v % 4, column lane % 32.
+    int *s_p = reinterpret_cast<int *>(&s_a[0][0]);
+    float *s_w = reinterpret_cast<float *>(&s_a[0][0]) + kTM;
+    if (!GATEUP) {
+        if (tid < kTM) {
+            s_p[tid] = my_p;
+            s_w[tid] = my_w;
+        }
+        __syncthreads();
+    }
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int m = m0 + mb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
             if (m >= m_end) continue;
             if (GATEUP) {
-                const float gv = acc[0][mb][v], uv = acc[NM - 1][mb][v];
+                const float gv = acc[0][mb][v], uv = acc[1][mb][v];
                 const float hv = gv * __builtin_amdgcn_rcpf(1.0f + expf(-gv)) * uv;
-                a.H[(int64_t)m * a.f + col] = __builtin_bit_cast(uint16_t, (f16)hv);
+                a.H[(int64_t)m * a.f + colb[0]] = __builtin_bit_cast(uint16_t, (f16)hv);
             } else {
-                const int p = a.perm[m];
-                a.Yb[(int64_t)p * a.d + col] = a.w[p] * acc[0][mb][v];
+                const int r = m - m0;
+                const int p = s_p[r];
+                const float wp = s_w[r];
+#pragma unroll
+                for (int n = 0; n < NB; ++n) a.Yb[(int64_t)p * a.d + colb[n]] = wp * acc[n][mb][v];
             }
         }
     }
+}
+
+template <int NB, bool GATEUP>
+__global__ __launch_bounds__(kGemmThreads, 2) void prefill_gemm_kernel(PrefillArgs a) {
+    static_assert(!GATEUP || NB == 2, "gate/up runs two B operands per wave");
+    constexpr int kCols = 4 * 32 * (GATEUP ? 1 : NB);
+    __shared__ __attribute__((aligned(16))) uint16_t s_a[2][kTM * kARow];
+    const int nN = (GATEUP ? a.f : a.d) / kCols;
+    // Work items in tile-major order (the column blocks of one M-tile, then
+    // the next tile of the same expert) cut into eight contiguous ranges, one
+    // per XCD (the hardware deals block b to XCD b % 8), so rows of x and
+    // weight slices are re-read from the XCD's own L2.
+    const int nwork = a.ntiles[0] * nN;
+    const int per = (nwork + 7) >> 3;
+    const int bi = blockIdx.x >> 3;
+    if (bi >= per) return;
+    const int wi = (blockIdx.x & 7) * per + bi;
+    if (wi >= nwork) return;
+    const int tile = wi / nN, nt = wi % nN;
+    const int e = a.tile_e[tile], m0 = a.tile_m0[tile];
+    const int m_end = a.off[e + 1];
+    const int rows = m_end - m0;
+    if (rows > 64)
+        prefill_tile<NB, GATEUP, 4>(a, s_a, e, m0, m_end, nt);
+    else if (rows > 32)
+        prefill_tile<NB, GATEUP, 2>(a, s_a, e, m0, m_end, nt);
+    else
+        prefill_tile<NB, GATEUP, 1>(a, s_a, e, m0, m_end, nt);
 }
 
 // ---------------------------------------------------------------------------
@@ -312,7 +420,7 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
 }
 
 struct PLayout {
-    size_t off, perm, ntiles, tile_e, tile_m0, H, Yb, total;
+    size_t off, perm, wsort, ntiles, tile_e, tile_m0, H, Yb, total;
     int max_tiles;
 };
 
@@ -325,6 +433,8 @@ PLayout prefill_layout(int T, int K, int E, int d, int f) {
     p = e0_align(p + sizeof(int32_t) * (E + 1));
     o.perm = p;
     p = e0_align(p + sizeof(int32_t) * (size_t)n);
+    o.wsort = p;
+    p = e0_align(p + sizeof(float) * (size_t)n);
     o.ntiles = p;
     p = e0_align(p + sizeof(int32_t));
     o.tile_e = p;
@@ -361,7 +471,7 @@ extern "C" e0_status e0_moe_sorted_prefill(const e0_moe_dims *dims, int32_t T, c
     E0_REQUIRE(dims && layer, E0_ERR_INVALID_ARG);
     const int d = dims->d_model, f = dims->d_ff, E = dims->n_experts, K = dims->top_k;
     E0_REQUIRE(T >= 0 && E >= 1 && K >= 1, E0_ERR_INVALID_ARG);
-    E0_REQUIRE(d > 0 && f > 0 && d % kTN == 0 && f % kTN == 0, E0_ERR_UNSUPPORTED_SHAPE);
+    E0_REQUIRE(d > 0 && f > 0 && d % 128 == 0 && f % 128 == 0, E0_ERR_UNSUPPORTED_SHAPE);
     E0_REQUIRE(K <= E && E <= 1024 && K <= 32, E0_ERR_UNSUPPORTED_SHAPE);
     const int64_t n = (int64_t)T * K;
     E0_REQUIRE(n <= (1 << 24), E0_ERR_CAPACITY);
@@ -391,6 +501,7 @@ extern "C" e0_status e0_moe_sorted_prefill(const e0_moe_dims *dims, int32_t T, c
     a.err = dev_err;
     a.off = reinterpret_cast<int32_t *>(wsb + lay.off);
     a.perm = reinterpret_cast<int32_t *>(wsb + lay.perm);
+    a.wsort = reinterpret_cast<float *>(wsb + lay.wsort);
     a.ntiles = reinterpret_cast<int32_t *>(wsb + lay.ntiles);
     a.tile_e = reinterpret_cast<int32_t *>(wsb + lay.tile_e);
     a.tile_m0 = reinterpret_cast<int32_t *>(wsb + lay.tile_m0);
@@ -402,9 +513,15 @@ extern "C" e0_status e0_moe_sorted_prefill(const e0_moe_dims *dims, int32_t T, c
     e0_status s;
     hipLaunchKernelGGL(prefill_sort_kernel, dim3(1), dim3(kSortThreads), 0, st, a);
     if ((s = e0_launch_status())) return s;
-    hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3(lay.max_tiles * (f / kTN)), dim3(kGemmThreads), 0, st, a);
+    // Grids cover the largest tile count in whole groups of eight blocks;
+    // blocks past the tiles the sort produced exit at once.
+    auto grid = [&](int cols) { return dim3((unsigned)((((int64_t)lay.max_tiles * (cols) + 7) / 8) * 8)); };
+    hipLaunchKernelGGL((prefill_gemm_kernel<2, true>), grid(f / 128), dim3(kGemmThreads), 0, st, a);
     if ((s = e0_launch_status())) return s;
-    hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3(lay.max_tiles * (d / kTN)), dim3(kGemmThreads), 0, st, a);
+    if (d % 256 == 0)
+        hipLaunchKernelGGL((prefill_gemm_kernel<2, false>), grid(d / 256), dim3(kGemmThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((prefill_gemm_kernel<1, false>), grid(d / 128), dim3(kGemmThreads), 0, st, a);
     if ((s = e0_launch_status())) return s;
     hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)(((int64_t)T * d / 4 + 255) / 256)), dim3(256), 0, st, a);
     return e0_launch_status();
