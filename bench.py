@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overlap", action="store_true", help="run the slot update on the decode stream")
     ap.add_argument("--cpu-steps", type=int, default=0, help="oracle sample size (0 = auto)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (the reference kernel for the "
+                         "FETCH_SIZE / WRITE_SIZE counter scale) and exit")
     return ap.parse_args()
 
 
@@ -369,6 +372,51 @@ def bench_prerouted(args, cfg, n_in):
                                           f"{L} layers"})
 
 
+# ---------------------------------------------------------------------------
+# HBM traffic of the dominant kernel, from committed counter passes
+# ---------------------------------------------------------------------------
+
+TRAFFIC_SOURCES = ("int4_gather_swiglu_amd/csrc/decode.hip", "int4_gather_swiglu_amd/csrc/e0_internal.h")
+
+
+def kernel_sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch of the decode kernel from the committed FETCH_SIZE /
+    WRITE_SIZE passes (profiles/hbm_traffic_<workload>.txt), or None when there
+    is no record or the kernel sources changed since it was taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    rec = [l for l in open(path).read().splitlines() if l.startswith("{")]
+    if not rec:
+        return None
+    d = json.loads(rec[-1])
+    if d.get("sources_sha256") != kernel_sources_digest():
+        return None
+    return int(d["hbm_bytes_per_launch"])
+
+
+def calibrate_copy(mib):
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                      "launches": 5}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -379,6 +427,9 @@ def main():
 
     from e0inputs import workloads as W
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     wl = args.workload
     cpu = None
     if wl == "decode35b":
@@ -403,6 +454,8 @@ def main():
            "data": "synthetic (seeded; int4 codes U{0..15}, fp16 scale U(0.005,0.02), bias -8s(1+U(-0.1,0.1)))",
            "config": res.pop("config")}
     out.update(res)
+    if wl != "prefill35b" and "roofline" in out:
+        out["roofline"]["traffic"] = recorded_traffic(wl)
     if not args.no_cpu_baseline and cpu is not None:
         out["cpu_baseline"] = cpu()
     print(json.dumps(out), flush=True)
