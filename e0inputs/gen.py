@@ -43,6 +43,8 @@ TAG_SHARED = 7        # ids: layer, matrix, part
 TAG_TARGETS = 8       # ids: step, owner layer
 TAG_PERM = 9          # ids: (none)
 TAG_REDRAW = 10       # ids: ... attempt
+TAG_NORM = 11         # ids: layer
+TAG_RESID = 12        # ids: step
 
 
 def _fin_int(z: int) -> int:

@@ -57,7 +57,12 @@ DECODE8_B32 = Config("decode8b_b32", 1004, d=2048, f=512, E=128, K=8, L=24, B=32
 PREROUTED35 = Config("prerouted35b", 1005, d=2048, f=512, E=256, K=4, L=32, B=1, steps=512, S=8,
                      heads=True, shared_f=512, lora_r=16, lora_alpha_over_r=2.0, repeat_p=0.7)
 
-ALL = {c.name: c for c in (TINY, DECODE35, PREFILL35, DECODE8_B1, DECODE8_B32, PREROUTED35)}
+# Chained decode: the 35B stack run as one token through all 40 layers, each
+# layer's input the norm of the residual after the previous one; routing given
+# per layer (standing in for the staged prediction).
+CHAIN35 = Config("chain35b", 1006, d=2048, f=512, E=256, K=4, L=40, B=1, steps=64, S=8)
+
+ALL = {c.name: c for c in (TINY, DECODE35, PREFILL35, DECODE8_B1, DECODE8_B32, PREROUTED35, CHAIN35)}
 HEAD_HIDDEN = 512
 
 
@@ -82,6 +87,17 @@ def activation_row(cfg: Config, step: int, layer: int, token: int, attempt: int)
     """One redrawn token row (used when a routing decision lacks margin)."""
     key = gen.stream_key(cfg.seed, gen.TAG_REDRAW, gen.TAG_ACT, step, layer, token, attempt)
     return gen.normal_f16(key, cfg.d)
+
+
+def norm_weight(cfg: Config, layer: int) -> np.ndarray:
+    """fp16 [d] norm gain of one layer: 1 + 0.1 N(0,1)."""
+    z = gen.normal(gen.stream_key(cfg.seed, gen.TAG_NORM, layer), cfg.d)
+    return (np.float32(1.0) + np.float32(0.1) * z).astype(np.float16)
+
+
+def residual0(cfg: Config, step: int) -> np.ndarray:
+    """fp32 [d] residual stream entering the first layer at a step; N(0,1)."""
+    return gen.normal(gen.stream_key(cfg.seed, gen.TAG_RESID, step), cfg.d).astype(np.float32)
 
 
 def router_weights(cfg: Config, layer: int) -> np.ndarray:

@@ -47,6 +47,8 @@ def lib():
         _LIB.orc_half.argtypes = [C.c_uint16]
         _LIB.orc_softmax_topk_margin.restype = C.c_double
         _LIB.orc_sigmoid_group_margin.restype = C.c_double
+        _LIB.orc_to_half.restype = C.c_uint16
+        _LIB.orc_to_half.argtypes = [C.c_double]
     return _LIB
 
 
@@ -239,3 +241,24 @@ def decode_layers(pools: Experts, S, slot_of, E, d, f, x, idx, w, n_threads=1):
     err = lib().orc_decode_layers(pools.ptr, S, _p(so), L, E, d, f, B, K, _p(x), _p(idx), _p(w), _p(y),
                                   n_threads)
     return y, err
+
+
+def to_half(v):
+    """Nearest binary16 bit patterns (ties to even) of float64 values."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    f = lib().orc_to_half
+    return np.array([f(C.c_double(float(t))) for t in v.ravel()], dtype=np.uint16).reshape(v.shape)
+
+
+def chain_decode(pools: Experts, S, slot_of, E, d, f, r0, g, eps, idx, w):
+    """Chained batch-1 decode: pools Experts of L*S entries (layer-major),
+    slot_of [L,E], r0 [d] (fp64), g fp16 [L,d], idx/w [L,K] ->
+    (y [L,d], r_out [L,d]) with r_out[l] the residual after layer l."""
+    so, idx, w = _c(slot_of, np.int32), _c(idx, np.int32), _c(w, np.float64)
+    r0, g = _c(r0, np.float64), _c(g, np.float16)
+    L, K = idx.shape
+    y = np.empty((L, d), dtype=np.float64)
+    r_out = np.empty((L, d), dtype=np.float64)
+    err = lib().orc_chain_decode(pools.ptr, S, _p(so), L, E, d, f, K, _p(r0), _p(g), C.c_double(eps), _p(idx),
+                                 _p(w), _p(y), _p(r_out))
+    return y, r_out, err

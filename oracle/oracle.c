@@ -605,3 +605,76 @@ int orc_decode_layers(const orc_expert *pools, int S, const int32_t *slot_of, in
     free(th);
     return err;
 }
+
+/* Round a double to the nearest IEEE binary16 value, ties to even (the
+ * conversion the fp16 activations of the path go through). Written from the
+ * format: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; values
+ * below 2^-14 are subnormal multiples of 2^-24; overflow gives infinity. */
+uint16_t orc_to_half(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7e00u);
+    if (a >= 65520.0) /* 65504 + half an ulp rounds up to infinity */
+        return (uint16_t)(sign | 0x7c00u);
+    int e;
+    frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+    int ex = e - 1; /* a in [2^ex, 2^(ex+1)) */
+    if (a == 0.0 || ex < -14)
+        ex = -14; /* subnormal range: spacing 2^-24 */
+    double ulp = ldexp(1.0, ex - 10);
+    double n = a / ulp; /* exact: a scaled by a power of two */
+    double r = nearbyint(n); /* current rounding mode: to nearest, ties to even */
+    uint32_t units = (uint32_t)r; /* multiples of ulp, at most 2048 */
+    uint32_t bits;
+    if (units >= 2048) { /* rounded up into the next binade */
+        ex += 1;
+        units >>= 1;
+    }
+    if (units < 1024) /* subnormal (only possible at ex == -14) */
+        bits = units;
+    else
+        bits = ((uint32_t)(ex + 15) << 10) | (units - 1024);
+    return (uint16_t)(sign | bits);
+}
+
+/* Chained batch-1 decode over L layers: the MoE input of layer l is the RMS
+ * norm of the residual stream, scaled by the layer's norm weight and rounded
+ * to fp16, and the layer's output is added back to the residual:
+ *   x_l = fp16( r_l / sqrt(mean(r_l^2) + eps) * g_l ),  y_l = MoE_l(x_l),
+ *   r_{l+1} = r_l + y_l.
+ * MoE_l is the staged path of layer l (pool layer l, slot_of row l). The
+ * pages run one token through the stacked layers with the next layers'
+ * weights staged ahead ([koala] Fig. 1 and its timeline); attention is not
+ * part of this path, so a layer here is norm + routed experts + residual.
+ * pools [L][S]; slot_of [L][E]; r0, g [L][d] (g fp16); idx, w [L][K];
+ * y, r_out [L][d] (r_out[l] = r_{l+1}). */
+int orc_chain_decode(const orc_expert *pools, int S, const int32_t *slot_of, int L, int E, int d, int f, int K,
+                     const double *r0, const uint16_t *g, double eps, const int32_t *idx, const double *w,
+                     double *y, double *r_out)
+{
+    int err = 0;
+    double *r = malloc(sizeof(double) * d);
+    uint16_t *x = malloc(sizeof(uint16_t) * d);
+    for (int i = 0; i < d; ++i)
+        r[i] = r0[i];
+    for (int l = 0; l < L; ++l) {
+        double ss = 0.0;
+        for (int i = 0; i < d; ++i)
+            ss += r[i] * r[i];
+        double inv = 1.0 / sqrt(ss / d + eps);
+        for (int i = 0; i < d; ++i)
+            x[i] = orc_to_half(r[i] * inv * orc_half(g[(size_t)l * d + i]));
+        double *yl = y + (size_t)l * d;
+        err |= orc_moe_staged(pools + (size_t)l * S, S, slot_of + (size_t)l * E, E, d, f, 1, K, x,
+                              idx + (size_t)l * K, w + (size_t)l * K, yl);
+        for (int i = 0; i < d; ++i) {
+            r[i] += yl[i];
+            r_out[(size_t)l * d + i] = r[i];
+        }
+    }
+    free(r);
+    free(x);
+    return err;
+}

@@ -101,6 +101,16 @@ int orc_decode_layers(const orc_expert *pools, int S, const int32_t *slot_of, in
                       int B, int K, const uint16_t *x, const int32_t *idx, const double *w, double *y,
                       int n_threads);
 
+/* Nearest IEEE binary16 of v, ties to even. */
+uint16_t orc_to_half(double v);
+
+/* Chained batch-1 decode: x_l = fp16(r_l / rms(r_l) * g_l), y_l = staged MoE
+ * of layer l on x_l, r_{l+1} = r_l + y_l. pools [L][S]; slot_of [L][E];
+ * r0 [d]; g fp16 [L][d]; idx, w [L][K]; y, r_out [L][d]. */
+int orc_chain_decode(const orc_expert *pools, int S, const int32_t *slot_of, int L, int E, int d, int f, int K,
+                     const double *r0, const uint16_t *g, double eps, const int32_t *idx, const double *w,
+                     double *y, double *r_out);
+
 #ifdef __cplusplus
 }
 #endif
