@@ -150,9 +150,16 @@ int32_t e0_abi_version(void);
 const char *e0_status_string(e0_status s);
 
 /* Operation ids for e0_workspace_bytes. */
-enum { E0_OP_ROUTE = 0, E0_OP_PREROUTER = 1, E0_OP_STAGED_DECODE = 2, E0_OP_SORTED_PREFILL = 3, E0_OP_SLOT_UPDATE = 4 };
+enum {
+    E0_OP_ROUTE = 0,
+    E0_OP_PREROUTER = 1,
+    E0_OP_STAGED_DECODE = 2,
+    E0_OP_SORTED_PREFILL = 3,
+    E0_OP_SLOT_UPDATE = 4,
+    E0_OP_CHAINED_DECODE = 5
+};
 
-/* Workspace bytes the call `op` needs. n = layers (decode, slot update),
+/* Workspace bytes the call `op` needs. n = layers (decode, chained decode, slot update),
  * tokens (prefill, route) or heads (prerouter); b = tokens per layer (decode,
  * slot update, prerouter), ignored otherwise; s = slots per layer (slot
  * update) or the shared expert's LoRA rank (decode; 0 = no LoRA), ignored
@@ -261,6 +268,38 @@ e0_status e0_slot_update(const e0_moe_dims *dims, int32_t L, int32_t B, int32_t 
                          const int32_t *cur_idx, int32_t *slot_of, int32_t *expert_of, const e0_stack *store,
                          const e0_stack *pool, int32_t *n_copied, void *ws, size_t ws_bytes, int32_t *dev_err,
                          void *stream);
+
+/*
+ * e0_moe_chained_decode — one token through L stacked layers in one call, the
+ * input of each layer computed from the output of the one before (the pages
+ * stage the next layers' experts ahead so that their weight reads overlap the
+ * current layer's compute: koala.ai.kr Fig. 1 and its timeline; the
+ * dependency that forces it, layer l+1's experts known only from layer l's
+ * output, is stated in the same page's problem section). A layer here is norm
+ * + routed experts + residual (attention is outside this path):
+ *   x_l = fp16( r_l / sqrt(mean_i r_l[i]^2 + eps) * g_l ),   r_0 = r_in,
+ *   y_l = sum_k w[l][k] * down(silu(gate(x_l)) * up(x_l)) of expert idx[l][k]
+ *         read through slot_of[l] from the pool (as e0_moe_staged_decode),
+ *   r_{l+1} = r_l + y_l.
+ * The routing of every layer is given up front (the staged prediction). The
+ * weights of later layers are requested while earlier layers compute.
+ *  r_in: device fp32 [d]; norm_w: device fp16 [L][d] (g_l); eps >= 0;
+ *  idx, w: device [L][K]; slot_of: device int32 [L][E]; pool: S slots per
+ *  layer; y: device fp32 [L][d], the MoE output of each layer; r_out: device
+ *  fp32 [L][d], r_out[l] = r_{l+1} (the last row is the stack's output). All
+ *  pointers 16-byte aligned except idx, w, slot_of, y.
+ *  ws: device workspace, e0_workspace_bytes(E0_OP_CHAINED_DECODE, dims, L, 0, 0)
+ *  (0 when the shape is unsupported).
+ *  dev_err: device int32, OR-ed with E0_DEV_BAD_ID / E0_DEV_NOT_RESIDENT (that
+ *  expert's contribution skipped) and E0_DEV_SYNC_TIMEOUT (an in-launch wait
+ *  of more than 50 ms; results then undefined).
+ *  Limits: d_model 2048; d_ff 256, 512 or 1024 (1024 with K <= 4); K <= 8;
+ *  E <= 1024. The caller owns every buffer; nothing is allocated or freed.
+ */
+e0_status e0_moe_chained_decode(const e0_moe_dims *dims, int32_t L, const float *r_in, const uint16_t *norm_w,
+                                float eps, const int32_t *idx, const float *w, const int32_t *slot_of, int32_t S,
+                                const e0_stack *pool, float *y, float *r_out, void *ws, size_t ws_bytes,
+                                int32_t *dev_err, void *stream);
 
 #ifdef __cplusplus
 }

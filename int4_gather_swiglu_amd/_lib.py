@@ -15,10 +15,11 @@ LIB_PATH = os.path.join(HERE, "libe0.so")
 
 E0_OK, E0_ERR_INVALID_ARG, E0_ERR_UNSUPPORTED_SHAPE, E0_ERR_CAPACITY, E0_ERR_HIP = range(5)
 E0_DEV_BAD_ID, E0_DEV_NOT_RESIDENT, E0_DEV_NO_SLOT = 1, 2, 4
-E0_OP_ROUTE, E0_OP_PREROUTER, E0_OP_STAGED_DECODE, E0_OP_SORTED_PREFILL, E0_OP_SLOT_UPDATE = range(5)
+(E0_OP_ROUTE, E0_OP_PREROUTER, E0_OP_STAGED_DECODE, E0_OP_SORTED_PREFILL, E0_OP_SLOT_UPDATE,
+ E0_OP_CHAINED_DECODE) = range(6)
 
 EXPORTS = ["e0_abi_version", "e0_status_string", "e0_workspace_bytes", "e0_route", "e0_prerouter",
-           "e0_moe_staged_decode", "e0_moe_sorted_prefill", "e0_slot_update"]
+           "e0_moe_staged_decode", "e0_moe_sorted_prefill", "e0_slot_update", "e0_moe_chained_decode"]
 
 
 class E0Error(RuntimeError):
@@ -82,7 +83,10 @@ def lib() -> C.CDLL:
                                             vp, vp]
         L.e0_slot_update.argtypes = [C.POINTER(MoeDims), i32, i32, i32, vp, vp, vp, vp, C.POINTER(Stack),
                                      C.POINTER(Stack), vp, vp, sz, vp, vp]
-        for n in ("e0_route", "e0_prerouter", "e0_moe_staged_decode", "e0_moe_sorted_prefill", "e0_slot_update"):
+        L.e0_moe_chained_decode.argtypes = [C.POINTER(MoeDims), i32, vp, vp, C.c_float, vp, vp, vp, i32,
+                                            C.POINTER(Stack), vp, vp, vp, sz, vp, vp]
+        for n in ("e0_route", "e0_prerouter", "e0_moe_staged_decode", "e0_moe_sorted_prefill", "e0_slot_update",
+                  "e0_moe_chained_decode"):
             getattr(L, n).restype = C.c_int32
         _LIB = L
     return _LIB
@@ -176,6 +180,14 @@ def e0_moe_staged_decode(dims: MoeDims, L: int, B: int, x, idx, w, slot_of, S: i
                                       C.byref(pool), C.byref(shared) if shared is not None else None, _ptr(y),
                                       _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
                                       _ptr(dev_err), _stream(stream)), "e0_moe_staged_decode")
+
+
+def e0_moe_chained_decode(dims: MoeDims, L: int, r_in, norm_w, eps: float, idx, w, slot_of, S: int, pool: Stack,
+                          y, r_out, ws, dev_err, stream=None):
+    _check(lib().e0_moe_chained_decode(C.byref(dims), L, _ptr(r_in), _ptr(norm_w), C.c_float(eps), _ptr(idx),
+                                       _ptr(w), _ptr(slot_of), S, C.byref(pool), _ptr(y), _ptr(r_out), _ptr(ws),
+                                       ws.numel() * ws.element_size() if ws is not None else 0, _ptr(dev_err),
+                                       _stream(stream)), "e0_moe_chained_decode")
 
 
 def e0_moe_sorted_prefill(dims: MoeDims, T: int, x, idx, w, layer: Stack, y, ws, dev_err, stream=None):

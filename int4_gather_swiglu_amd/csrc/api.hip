@@ -8,6 +8,7 @@ size_t e0_decode_workspace_bytes(const e0_moe_dims *dims, int32_t L, int32_t B, 
 size_t e0_slot_workspace_bytes(const e0_moe_dims *dims, int32_t L, int32_t B, int32_t S);
 size_t e0_prerouter_workspace_bytes(int32_t H, int32_t B, int32_t E, int32_t hid);
 size_t e0_prefill_workspace_bytes(const e0_moe_dims *dims, int32_t T);
+size_t e0_chain_workspace_bytes(const e0_moe_dims *dims, int32_t L);
 
 extern "C" int32_t e0_abi_version(void) { return E0_ABI_VERSION; }
 
@@ -44,6 +45,7 @@ extern "C" size_t e0_workspace_bytes(int32_t op, const e0_moe_dims *dims, int32_
         case E0_OP_STAGED_DECODE: return e0_decode_workspace_bytes(dims, n, b, s);
         case E0_OP_SORTED_PREFILL: return e0_prefill_workspace_bytes(dims, n);
         case E0_OP_SLOT_UPDATE: return e0_slot_workspace_bytes(dims, n, b, s);
+        case E0_OP_CHAINED_DECODE: return e0_chain_workspace_bytes(dims, n);
         default: return 0;
     }
 }

@@ -84,6 +84,14 @@ struct DecodeArgs {
     int n_gu;         // gate/up items per layer (units * d_ff / 64)
     int n_dn;         // down items per layer
     int lag;          // the down items of layer l follow the gate/up items of layer l + lag
+    // chained decode (batch 1): the input of layer l is the normed residual,
+    // and layer l's down items add its output to the residual
+    int chain;
+    const float *r_in;       // [d] residual entering layer 0
+    float *r_out;            // [L][d] residual after each layer
+    const uint16_t *norm_w;  // [L][d] fp16 norm gains
+    float norm_eps;
+    uint64_t *dflags;        // [L][n_dn] down items of the chain
 };
 
 E0_DEV int pairs_per_layer(const DecodeArgs &a) { return a.B * a.K + a.B; }
@@ -955,6 +963,55 @@ E0_DEV void fused_lora_item(const DecodeArgs &a, int l) {
     signal_ready(a.flags + l, a.epoch);
 }
 
+// Chained decode: the fp16 input slice of this lane (inputs 32 lane .. +31)
+// of layer l, x = fp16(r / sqrt(mean(r^2) + eps) * g), r the residual after
+// layer l - 1 (the call's input for layer 0). Waits (whole workgroup) for the
+// down items of layer l - 1, which publish the residual.
+E0_DEV void chain_input(const DecodeArgs &a, int l, u32x4 (&xr)[4]) {
+    const int lane = threadIdx.x & 63;
+    const int d = a.d;
+    u32x4 gv[4];
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd)
+        gv[wd] = *reinterpret_cast<const u32x4 *>(a.norm_w + (int64_t)l * d + lane * 32 + wd * 8);
+    float rv[32];
+    if (l == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(a.r_in + lane * 32 + 4 * i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rv[4 * i + j] = v[j];
+        }
+    } else {
+        if (!wait_ready(a.dflags + (int64_t)(l - 1) * a.n_dn, a.n_dn, a.epoch) && threadIdx.x == 0)
+            set_err(a.err, E0_DEV_SYNC_TIMEOUT);
+        const uint64_t *src = reinterpret_cast<const uint64_t *>(a.r_out + (int64_t)(l - 1) * d + lane * 32);
+        uint64_t t[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) t[i] = coherent_load(src + i);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            rv[2 * i] = __builtin_bit_cast(float, (uint32_t)t[i]);
+            rv[2 * i + 1] = __builtin_bit_cast(float, (uint32_t)(t[i] >> 32));
+        }
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) ss += rv[i] * rv[i];
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)d + a.norm_eps);
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f16x2 g2 = as_h2(gv[wd][j]);
+            const f16 x0 = (f16)(rv[8 * wd + 2 * j] * inv * (float)g2[0]);
+            const f16 x1 = (f16)(rv[8 * wd + 2 * j + 1] * inv * (float)g2[1]);
+            xr[wd][j] = (uint32_t)__builtin_bit_cast(uint16_t, x0) | ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
+        }
+    }
+}
+
 // Slot of routed expert k of layer l (batch 1), or -1 with the reason in
 // `bits` (E0_DEV_BAD_ID / E0_DEV_NOT_RESIDENT). The result is wave-uniform.
 E0_DEV int routed_slot(const DecodeArgs &a, int l, int k, int &bits) {
@@ -1041,11 +1098,16 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *
         load(0, A);
         load(1, B);
         u32x4 xr[NP][4];
+        if constexpr (NP == 1 && !SHARED) {
+            if (a.chain) chain_input(a, l, xr[0]);
+        }
+        if (!a.chain) {
 #pragma unroll
-        for (int np = 0; np < NP; ++np)
+            for (int np = 0; np < NP; ++np)
 #pragma unroll
-            for (int wd = 0; wd < 4; ++wd)
-                xr[np][wd] = *reinterpret_cast<const u32x4 *>(a.x + (int64_t)l * d + (np * 64 + lane) * 32 + wd * 8);
+                for (int wd = 0; wd < 4; ++wd)
+                    xr[np][wd] = *reinterpret_cast<const u32x4 *>(a.x + (int64_t)l * d + (np * 64 + lane) * 32 + wd * 8);
+        }
         uint32_t xp[NP][4][4];
         float xs[NP];
 #pragma unroll
@@ -1289,8 +1351,15 @@ E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, 
             for (int i = 0; i < a.r; ++i) dl += h2f(brow[i]) * s_lora[i];
             v += a.lscale * dl;
         }
-        if (gl == 0) a.y[(int64_t)l * d + row] = v;
+        if (gl == 0) {
+            a.y[(int64_t)l * d + row] = v;
+            if (a.chain) {
+                const float rp = l == 0 ? a.r_in[row] : coherent_load(a.r_out + (int64_t)(l - 1) * d + row);
+                coherent_store(a.r_out + (int64_t)l * d + row, rp + v);
+            }
+        }
     }
+    if (a.chain) signal_ready(a.dflags + (int64_t)l * a.n_dn + rb, a.epoch);
 }
 
 template <int NP, int LPR, int KM, int RW>
@@ -1361,10 +1430,15 @@ int d_lpr(int d, int &np) {
 int f_lpr(int f) { return (f >= 128 && f <= 2048 && pow2(f)) ? f / 32 : 0; }
 
 struct Layout {
-    size_t ucnt, uexp, uslot, uoff, pairs, hbuf, lora, flags, hblk, total;
+    size_t ucnt, uexp, uslot, uoff, pairs, hbuf, lora, flags, hblk, dflags, total;
 };
 
-Layout decode_layout(int L, int B, int K, int E, int f, int r) {
+// Output rows per wavefront of a down item of the single-launch kernel: at
+// least two load instructions per unit, so its scales are one 4/8/16-byte load.
+int fused_rows_per_wave(int K, int lpr_f) { return (K <= 4 || lpr_f == 8) ? 16 : 8; }
+
+// n_dn: down items per layer of a chained call (their ready flags), else 0.
+Layout decode_layout(int L, int B, int K, int E, int f, int r, int n_dn = 0) {
     Layout o;
     const int umax = B == 1 ? K : (E < B * K ? E : B * K);
     size_t off = 0;
@@ -1386,6 +1460,8 @@ Layout decode_layout(int L, int B, int K, int E, int f, int r) {
     off = e0_align(off + (B == 1 ? sizeof(uint64_t) * (size_t)L * (1 + (K + 1) * (size_t)(f / kHalfBlk)) : 0));
     o.hblk = off;
     off = e0_align(off + (B == 1 ? sizeof(uint32_t) * (size_t)L * (K + 1) * (size_t)(f / 32) * kBlk : 0));
+    o.dflags = off;
+    off = e0_align(off + sizeof(uint64_t) * (size_t)L * n_dn);
     o.total = off;
     return o;
 }
@@ -1423,6 +1499,31 @@ bool dispatch_down(int lpr, const DecodeArgs &a, dim3 grid, hipStream_t st) {
         case 64: hipLaunchKernelGGL(decode_down_kernel<64>, grid, dim3(kThreads), 0, st, a); return true;
         default: return false;
     }
+}
+
+void launch_fused(const DecodeArgs &a, int lpr_f, bool small, dim3 grid, hipStream_t st) {
+    switch (lpr_f) {
+        case 8:
+            if (small) hipLaunchKernelGGL((decode_fused_kernel<1, 8, 4, 16>), grid, dim3(kFuseThreads), 0, st, a);
+            else hipLaunchKernelGGL((decode_fused_kernel<1, 8, 8, 16>), grid, dim3(kFuseThreads), 0, st, a);
+            break;
+        case 16:
+            if (small) hipLaunchKernelGGL((decode_fused_kernel<1, 16, 4, 16>), grid, dim3(kFuseThreads), 0, st, a);
+            else hipLaunchKernelGGL((decode_fused_kernel<1, 16, 8, 8>), grid, dim3(kFuseThreads), 0, st, a);
+            break;
+        default:
+            hipLaunchKernelGGL((decode_fused_kernel<1, 32, 4, 16>), grid, dim3(kFuseThreads), 0, st, a);
+            break;
+    }
+}
+
+// Shapes the single-launch batch-1 kernel takes: d_model 2048 and the listed
+// d_ff / top-K combinations.
+bool fused_shape_ok(int d, int f, int K) {
+    int np = 0;
+    const int lpr_d = d_lpr(d, np), lpr_f = f_lpr(f);
+    return lpr_d == 64 && np == 1 && (lpr_f == 8 || lpr_f == 16 || (lpr_f == 32 && K <= 4)) && K <= 8 &&
+           f % (kHalfBlk * kFuseWaves) == 0;
 }
 
 bool stack_ok(const e0_stack *s, int first, int last) {
@@ -1528,9 +1629,7 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
         a.nch = f / kHalfBlk;
         a.n_lora = (a.has_shared && r > 0) ? L : 0;
         const bool small = K <= 4;
-        // output rows per wavefront of a down item (at least two load
-        // instructions per unit, so its scales are one 4/8/16-byte load)
-        const int rw = (small || lpr_f == 8) ? 16 : 8;
+        const int rw = fused_rows_per_wave(K, lpr_f);
         const int64_t n_gu = (int64_t)U * (a.nch / kFuseWaves), n_dn = d / (kFuseWaves * rw);  // per layer
         E0_REQUIRE(a.n_lora + L * (n_gu + n_dn) <= (int64_t)INT32_MAX, E0_ERR_CAPACITY);
         a.n_gu = (int)n_gu;
@@ -1546,19 +1645,7 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
         const int64_t lag = (6 * (int64_t)cus + n_gu + n_dn - 1) / (n_gu + n_dn) + 1;
         a.lag = (int)(lag < L ? lag : L);
         const dim3 grid((unsigned)(a.n_lora + L * (n_gu + n_dn)));
-        switch (lpr_f) {
-            case 8:
-                if (small) hipLaunchKernelGGL((decode_fused_kernel<1, 8, 4, 16>), grid, dim3(kFuseThreads), 0, st, a);
-                else hipLaunchKernelGGL((decode_fused_kernel<1, 8, 8, 16>), grid, dim3(kFuseThreads), 0, st, a);
-                break;
-            case 16:
-                if (small) hipLaunchKernelGGL((decode_fused_kernel<1, 16, 4, 16>), grid, dim3(kFuseThreads), 0, st, a);
-                else hipLaunchKernelGGL((decode_fused_kernel<1, 16, 8, 8>), grid, dim3(kFuseThreads), 0, st, a);
-                break;
-            default:
-                hipLaunchKernelGGL((decode_fused_kernel<1, 32, 4, 16>), grid, dim3(kFuseThreads), 0, st, a);
-                break;
-        }
+        launch_fused(a, lpr_f, small, grid, st);
         return e0_launch_status();
     }
     if (a.has_plan) {
@@ -1608,5 +1695,72 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
     }
     if ((s = e0_launch_status())) return s;
     E0_REQUIRE(dispatch_down(lpr_f, a, dim3(L, (d + kDownRows - 1) / kDownRows), st), E0_ERR_UNSUPPORTED_SHAPE);
+    return e0_launch_status();
+}
+
+size_t e0_chain_workspace_bytes(const e0_moe_dims *dims, int32_t L) {
+    if (!dims || L < 0 || !fused_shape_ok(dims->d_model, dims->d_ff, dims->top_k)) return 0;
+    const int n_dn = dims->d_model / (kFuseWaves * fused_rows_per_wave(dims->top_k, f_lpr(dims->d_ff)));
+    return decode_layout(L, 1, dims->top_k, dims->n_experts, dims->d_ff, 0, n_dn).total;
+}
+
+extern "C" e0_status e0_moe_chained_decode(const e0_moe_dims *dims, int32_t L, const float *r_in, const uint16_t *norm_w,
+                                           float eps, const int32_t *idx, const float *w, const int32_t *slot_of,
+                                           int32_t S, const e0_stack *pool, float *y, float *r_out, void *ws,
+                                           size_t ws_bytes, int32_t *dev_err, void *stream) {
+    E0_REQUIRE(dims && pool, E0_ERR_INVALID_ARG);
+    const int d = dims->d_model, f = dims->d_ff, E = dims->n_experts, K = dims->top_k;
+    E0_REQUIRE(L >= 0 && S >= 1 && E >= 1 && K >= 1 && K <= E && E <= kMaxE, E0_ERR_INVALID_ARG);
+    E0_REQUIRE(fused_shape_ok(d, f, K), E0_ERR_UNSUPPORTED_SHAPE);
+    E0_REQUIRE(isfinite(eps) && eps >= 0.0f, E0_ERR_INVALID_ARG);
+    E0_REQUIRE(r_in && norm_w && idx && w && slot_of && y && r_out && dev_err, E0_ERR_INVALID_ARG);
+    E0_REQUIRE(((reinterpret_cast<uintptr_t>(r_in) | reinterpret_cast<uintptr_t>(norm_w) |
+                 reinterpret_cast<uintptr_t>(r_out)) & 15) == 0, E0_ERR_INVALID_ARG);
+    E0_REQUIRE(stack_ok(pool, 0, 8), E0_ERR_INVALID_ARG);
+    const int lpr_f = f_lpr(f);
+    const int rw = fused_rows_per_wave(K, lpr_f);
+    const int64_t n_gu = (int64_t)K * (f / kHalfBlk / kFuseWaves), n_dn = d / (kFuseWaves * rw);
+    const Layout lay = decode_layout(L, 1, K, E, f, 0, (int)n_dn);
+    E0_REQUIRE(ws && ws_bytes >= lay.total && (reinterpret_cast<uintptr_t>(ws) & 255) == 0, E0_ERR_CAPACITY);
+    E0_REQUIRE((int64_t)L * (n_gu + n_dn) <= (int64_t)INT32_MAX, E0_ERR_CAPACITY);
+    if (L == 0) return E0_OK;
+
+    DecodeArgs a{};
+    a.L = L;
+    a.B = 1;
+    a.K = K;
+    a.E = E;
+    a.S = S;
+    a.d = d;
+    a.f = f;
+    a.idx = idx;
+    a.w = w;
+    a.slot_of = slot_of;
+    a.pool = to_stack(*pool);
+    a.y = y;
+    a.err = dev_err;
+    a.umax = K;
+    char *wsb = static_cast<char *>(ws);
+    a.hbuf = reinterpret_cast<float *>(wsb + lay.hbuf);
+    a.lora_a = reinterpret_cast<float *>(wsb + lay.lora);
+    a.flags = reinterpret_cast<uint64_t *>(wsb + lay.flags);
+    a.hblk = reinterpret_cast<uint32_t *>(wsb + lay.hblk);
+    a.epoch = e0_next_epoch();
+    a.units = K;
+    a.nch = f / kHalfBlk;
+    a.n_lora = 0;
+    a.n_gu = (int)n_gu;
+    a.n_dn = (int)n_dn;
+    // Layer l's down items follow its gate/up items directly; the gate/up
+    // items of layer l + 1 follow them and wait for them, so every wait is on
+    // items dispatched earlier.
+    a.lag = 0;
+    a.chain = 1;
+    a.r_in = r_in;
+    a.r_out = r_out;
+    a.norm_w = norm_w;
+    a.norm_eps = eps;
+    a.dflags = reinterpret_cast<uint64_t *>(wsb + lay.dflags);
+    launch_fused(a, lpr_f, K <= 4, dim3((unsigned)(L * (n_gu + n_dn))), static_cast<hipStream_t>(stream));
     return e0_launch_status();
 }
