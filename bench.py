@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode35b",
-                    choices=["decode35b", "prefill35b", "decode8b_b1", "decode8b_b32", "prerouted35b"])
+                    choices=["decode35b", "prefill35b", "decode8b_b1", "decode8b_b32", "prerouted35b", "chain35b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overlap", action="store_true", help="run the slot update on the decode stream")
     ap.add_argument("--cpu-steps", type=int, default=0, help="oracle sample size (0 = auto)")
@@ -86,7 +86,7 @@ def run_steps(args, step):
 # staged decode (35B and 8B tiers)
 # ---------------------------------------------------------------------------
 
-def bench_decode(args, cfg, n_in):
+def bench_decode(args, cfg, n_in, chain=False):
     import torch
 
     from e0inputs import gen, gpu as G, workloads as W
@@ -111,6 +111,10 @@ def bench_decode(args, cfg, n_in):
         logits = torch.from_numpy(np.stack([np.stack([W.given_logits(cfg, t, l) for l in range(L)])
                                             for t in range(n_in)]).view(np.int16)).to(dev)
     y = torch.empty((L, B, d), dtype=torch.float32, device=dev)
+    if chain:
+        r_ins = torch.from_numpy(np.stack([W.residual0(cfg, t) for t in range(n_in)])).to(dev)
+        norm_w = torch.from_numpy(np.stack([W.norm_weight(cfg, l) for l in range(L)]).view(np.int16)).to(dev)
+        r_out = torch.empty((L, d), dtype=torch.float32, device=dev)
     dims = E.moe_dims(d, f, Ex, K)
     pipe = StagedPipeline(dims, L, B, S, E.stack_from_bundles(store, d, f, bb, Ex * bb),
                           E.stack_from_bundles(pool, d, f, bb, S * bb), device=dev, side_stream=not args.no_overlap)
@@ -137,7 +141,10 @@ def bench_decode(args, cfg, n_in):
         if rec is not None:
             ev_upd[rec][1].record(pipe.side)
             ev_dec[rec][0].record(pipe.main)
-        pipe.decode(cb, xs[t % n_in], y)
+        if chain:
+            pipe.decode_chain(cb, r_ins[t % n_in], norm_w, CHAIN_EPS, y, r_out)
+        else:
+            pipe.decode(cb, xs[t % n_in], y)
         if rec is not None:
             ev_dec[rec][1].record(pipe.main)
         pipe.join()
@@ -158,18 +165,52 @@ def bench_decode(args, cfg, n_in):
     achieved = algo_bytes / (dec_ms * 1e-3) / 1e9
     return dict(value=round(args.steps * B / wall, 2), unit=f"tok/s ({L}-layer MoE stack, batch {B})",
                 ms_per_step=round(wall * 1e3 / args.steps, 5),
-                config={"workload": f"{cfg.name}: staged decode, {L} layers x {Ex} experts, d_model {d}, d_ff {f}, "
+                config={"workload": f"{cfg.name}: {'chained' if chain else 'staged'} decode, {L} layers x {Ex} "
+                                    f"experts, d_model {d}, d_ff {f}, "
                                     f"{'sigmoid-group' if cfg.mode else 'softmax'} top-{K}, batch {B}, "
-                                    f"{S} slots/layer",
+                                    f"{S} slots/layer" + (", layer input = RMS norm of the residual" if chain else ""),
                         "layers": L, "experts": Ex, "d_model": d, "d_ff": f, "top_k": K, "batch": B, "slots": S},
                 layer_tok_per_s=round(args.steps * B * L / wall, 1),
                 decode_call_us=round(dec_ms * 1e3, 2), route_and_slot_update_us=round(upd_ms * 1e3, 2),
                 slot_copies_last_step=int(pipe.n_copied.sum().item()), overlap=not args.no_overlap,
-                roofline={"bound": "hbm", "kernel": "e0_moe_staged_decode (gate/up + down launches)",
+                roofline={"bound": "hbm",
+                          "kernel": ("e0_moe_chained_decode (one launch)" if chain else
+                                     "e0_moe_staged_decode (one launch)" if B == 1 else
+                                     "e0_moe_staged_decode (plan + gate/up + down launches)"),
                           "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                           "algorithmic_bytes_per_launch": algo_bytes,
                           "unit_of_work": f"{np.mean(uniq):.2f} distinct experts x {bb} B per layer, {L} layers"})
+
+
+CHAIN_EPS = 1e-6
+
+
+def cpu_chain(cfg, n_steps):
+    """Oracle chained decode (norm -> staged MoE -> residual per layer) on a
+    sample of steps; one thread (each layer needs the one before)."""
+    import oracle
+    from e0inputs import gen, workloads as W
+
+    steps = n_steps or 2
+    g = np.stack([W.norm_weight(cfg, l) for l in range(cfg.L)])
+    t_total = 0.0
+    for t in range(steps):
+        lg = np.stack([W.given_logits(cfg, t, l)[0] for l in range(cfg.L)]).astype(np.float32)
+        idx, w = oracle.softmax_topk(lg, cfg.K)
+        mats, so = [], np.full((cfg.L, cfg.E), -1, np.int32)
+        for l in range(cfg.L):
+            for s_, e in enumerate(int(v) for v in idx[l]):
+                mats.append(gen.expert(cfg.seed, l, e, cfg.d, cfg.f))
+                so[l, e] = s_
+        t0 = time.perf_counter()
+        oracle.chain_decode(oracle.Experts(mats), cfg.K, so, cfg.E, cfg.d, cfg.f,
+                            W.residual0(cfg, t).astype(np.float64), g, CHAIN_EPS, idx, w)
+        t_total += time.perf_counter() - t0
+    return {"value": round(steps / t_total, 4), "unit": f"tok/s ({cfg.L}-layer chained stack, batch 1)",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{steps} token(s) through {cfg.L} chained layers: the fp64 C oracle's chained decode, "
+                      f"1 thread; {t_total:.1f} s"}
 
 
 def cpu_decode(cfg, n_steps):
@@ -444,6 +485,9 @@ def main():
     elif wl == "decode8b_b32":
         res = bench_decode(args, W.DECODE8_B32, 8)
         cpu = (lambda: cpu_decode(W.DECODE8_B32, args.cpu_steps))
+    elif wl == "chain35b":
+        res = bench_decode(args, W.CHAIN35, 16, chain=True)
+        cpu = (lambda: cpu_chain(W.CHAIN35, args.cpu_steps))
     else:
         res = bench_prerouted(args, W.PREROUTED35, 32)
     out = {"metric": METRIC, "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1, "steps": args.steps,

@@ -89,6 +89,17 @@ class StagedPipeline:
     def decode(self, buf: int, x, y):
         self.decode_ids(self.idx[buf], self.w[buf], x, y)
 
+    def decode_chain(self, buf: int, r_in, norm_w, eps: float, y, r_out):
+        """Chained decode of one token through the L layers (batch 1): layer
+        l's input is the normed residual after layer l - 1."""
+        if getattr(self, "ws_chain", None) is None:
+            n = E.workspace_bytes(E.E0_OP_CHAINED_DECODE, self.dims, self.L)
+            if n == 0:
+                raise E.E0Error(E.E0_ERR_UNSUPPORTED_SHAPE, "e0_moe_chained_decode")
+            self.ws_chain = torch.empty(n, dtype=torch.uint8, device=self.dev)
+        E.e0_moe_chained_decode(self.dims, self.L, r_in, norm_w, eps, self.idx[buf], self.w[buf], self.slot_of, self.S,
+                                self.pool, y, r_out, self.ws_chain, self.err, stream=self.main)
+
 
 class PrerouterPipeline(StagedPipeline):
     """Staged decode whose routing is the prerouter heads' prediction.
