@@ -1027,7 +1027,7 @@ E0_DEV int routed_slot(const DecodeArgs &a, int l, int k, int &bits) {
 // units, streamed in 4 batches of 4 units with the loads of the next batch in
 // flight while one is computed. It publishes its half block with its own
 // flag, so the wavefronts of an item never wait on each other.
-template <int NP, bool SHARED>
+template <int NP, bool SHARED, bool CHAIN = false>
 E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *s_small) {
     constexpr int NBT = 16 / kFlatBatch;  // batches per half block
     const int lane = threadIdx.x & 63, wv = wave_id();
@@ -1094,14 +1094,18 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *
                 }
             }
         };
-        Stage A, B;
+        Stage A, B, C, D;  // C, D: chained items only
         load(0, A);
         load(1, B);
         u32x4 xr[NP][4];
-        if constexpr (NP == 1 && !SHARED) {
-            if (a.chain) chain_input(a, l, xr[0]);
-        }
-        if (!a.chain) {
+        if constexpr (CHAIN) {
+            // Chained: every batch's weights are requested before the wait for
+            // the previous layer, so none of them is on the critical path.
+            static_assert(NP == 1 && !SHARED && NBT == 4, "chained items: d_model 2048, routed experts");
+            load(2, C);
+            load(3, D);
+            chain_input(a, l, xr[0]);
+        } else {
 #pragma unroll
             for (int np = 0; np < NP; ++np)
 #pragma unroll
@@ -1151,19 +1155,26 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *
             const float other = __shfl_xor(val, 32);
             if (m == 0 && lane % DUP == 0) s_hv[bt * kFlatBatch + rr] = silu(val) * other;
         };
-        // Two-stage pipeline; the empty asm statements keep the compiler from
-        // hoisting later batches' loads (register pressure) or sinking them.
+        if constexpr (CHAIN) {
+            compute(0, A);
+            compute(1, B);
+            compute(2, C);
+            compute(3, D);
+        } else {
+            // Two-stage pipeline; the empty asm statements keep the compiler from
+            // hoisting later batches' loads (register pressure) or sinking them.
 #pragma unroll
-        for (int bt = 0; bt < NBT; ++bt) {
-            __asm__ __volatile__("" ::: "memory");
-            if (bt & 1) {
-                compute(bt, B);
+            for (int bt = 0; bt < NBT; ++bt) {
                 __asm__ __volatile__("" ::: "memory");
-                if (bt + 2 < NBT) load(bt + 2, B);
-            } else {
-                compute(bt, A);
-                __asm__ __volatile__("" ::: "memory");
-                if (bt + 2 < NBT) load(bt + 2, A);
+                if (bt & 1) {
+                    compute(bt, B);
+                    __asm__ __volatile__("" ::: "memory");
+                    if (bt + 2 < NBT) load(bt + 2, B);
+                } else {
+                    compute(bt, A);
+                    __asm__ __volatile__("" ::: "memory");
+                    if (bt + 2 < NBT) load(bt + 2, A);
+                }
             }
         }
     } else if (lane < 16) {
@@ -1207,7 +1218,7 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *
 
 // Down rows: LPR lanes per row (d_ff = 32 * LPR), KM routed units at most
 // plus the shared expert, RW output rows per wavefront (kFuseWaves * RW per item).
-template <int LPR, int KM, int RW>
+template <int LPR, int KM, int RW, bool CHAIN = false>
 E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, float *s_hsh, float *s_lora) {
     constexpr int RPI = kWave / LPR;  // rows per load instruction
     constexpr int IT = RW / RPI;      // load instructions per unit
@@ -1298,6 +1309,14 @@ E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, 
     const bool lora = a.has_shared && a.r > 0;
     if (lora)
         for (int i = threadIdx.x; i < f; i += kFuseThreads) s_hsh[i] = coherent_load(hrow(a, l, K) + i);
+    // Chained: the residual rows this lane group adds to, requested with the
+    // staging loads (layer l - 1 finished before any gate/up item of l ran).
+    float rprev[IT];
+    if constexpr (CHAIN) {
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+            rprev[it] = l == 0 ? a.r_in[rows0 + it] : coherent_load(a.r_out + (int64_t)(l - 1) * d + rows0 + it);
+    }
     __syncthreads();
     if (lora) {
         // A_down h_shared.
@@ -1353,16 +1372,13 @@ E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, 
         }
         if (gl == 0) {
             a.y[(int64_t)l * d + row] = v;
-            if (a.chain) {
-                const float rp = l == 0 ? a.r_in[row] : coherent_load(a.r_out + (int64_t)(l - 1) * d + row);
-                coherent_store(a.r_out + (int64_t)l * d + row, rp + v);
-            }
+            if constexpr (CHAIN) coherent_store(a.r_out + (int64_t)l * d + row, rprev[it] + v);
         }
     }
-    if (a.chain) signal_ready(a.dflags + (int64_t)l * a.n_dn + rb, a.epoch);
+    if constexpr (CHAIN) signal_ready(a.dflags + (int64_t)l * a.n_dn + rb, a.epoch);
 }
 
-template <int NP, int LPR, int KM, int RW>
+template <int NP, int LPR, int KM, int RW, bool CHAIN = false>
 __global__ __launch_bounds__(kFuseThreads) void decode_fused_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t s_hb[(KM + 1) * LPR * kBlk];
     __shared__ float s_hsh[32 * LPR];
@@ -1399,12 +1415,14 @@ __global__ __launch_bounds__(kFuseThreads) void decode_fused_kernel(DecodeArgs a
     if (gu) {
         const int per_u = a.nch / kFuseWaves;  // items per unit
         const int u = r / per_u, cg = r % per_u;
-        if (u < a.K)
+        if constexpr (CHAIN)
+            fused_gateup_item<NP, false, true>(a, l, u, cg, s_small);
+        else if (u < a.K)
             fused_gateup_item<NP, false>(a, l, u, cg, s_small);
         else
             fused_gateup_item<NP, true>(a, l, u, cg, s_small);
     } else {
-        fused_down_item<LPR, KM, RW>(a, l, r, s_hb, s_hsh, s_small);
+        fused_down_item<LPR, KM, RW, CHAIN>(a, l, r, s_hb, s_hsh, s_small);
     }
 }
 
@@ -1502,6 +1520,22 @@ bool dispatch_down(int lpr, const DecodeArgs &a, dim3 grid, hipStream_t st) {
 }
 
 void launch_fused(const DecodeArgs &a, int lpr_f, bool small, dim3 grid, hipStream_t st) {
+    if (a.chain) {
+        switch (lpr_f) {
+            case 8:
+                if (small) hipLaunchKernelGGL((decode_fused_kernel<1, 8, 4, 16, true>), grid, dim3(kFuseThreads), 0, st, a);
+                else hipLaunchKernelGGL((decode_fused_kernel<1, 8, 8, 16, true>), grid, dim3(kFuseThreads), 0, st, a);
+                break;
+            case 16:
+                if (small) hipLaunchKernelGGL((decode_fused_kernel<1, 16, 4, 16, true>), grid, dim3(kFuseThreads), 0, st, a);
+                else hipLaunchKernelGGL((decode_fused_kernel<1, 16, 8, 8, true>), grid, dim3(kFuseThreads), 0, st, a);
+                break;
+            default:
+                hipLaunchKernelGGL((decode_fused_kernel<1, 32, 4, 16, true>), grid, dim3(kFuseThreads), 0, st, a);
+                break;
+        }
+        return;
+    }
     switch (lpr_f) {
         case 8:
             if (small) hipLaunchKernelGGL((decode_fused_kernel<1, 8, 4, 16>), grid, dim3(kFuseThreads), 0, st, a);
