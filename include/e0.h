@@ -257,8 +257,14 @@ e0_status e0_moe_sorted_prefill(const e0_moe_dims *dims, int32_t T, const uint16
  *   step) a free slot always exists and no slot read by the step in flight is
  *   written, so this may run on a side stream concurrently with that step.
  *  next_idx, cur_idx: device int32 [L][B][K]; slot_of: device [L][E];
- *  expert_of: device [L][S] (-1 = empty); store: slot e = expert e; pool: S
- *  slots. n_copied: optional device int32 [L], experts copied per layer.
+ *  expert_of: device [L][S] (-1 = empty); store: slot e = expert e, in device
+ *  memory or in pinned host memory mapped for the device (hipHostMalloc; the
+ *  copy then reads it over the host link: the store outside HBM with the pool
+ *  as its cache, the pages' own setting with the SSD replaced by host DRAM);
+ *  each part's address is resolved with hipPointerGetAttributes and a part the
+ *  device cannot reach fails the call with E0_ERR_INVALID_ARG before anything
+ *  is enqueued; pool: S slots in device memory. n_copied: optional device
+ *  int32 [L], experts copied per layer.
  *  ws: device workspace, e0_workspace_bytes(E0_OP_SLOT_UPDATE, dims, L, B, S).
  *  dev_err: OR-ed with E0_DEV_BAD_ID, E0_DEV_NO_SLOT (then the experts that
  *  found a slot are still placed, the others are not).

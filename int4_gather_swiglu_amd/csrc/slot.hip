@@ -233,6 +233,25 @@ SlotLayout slot_layout(int L, int BK, int S, int E) {
     return o;
 }
 
+// The store may live in device memory or in pinned host memory mapped for
+// the device (then the copy pulls the changed experts over the host link).
+// Each part's address is resolved to the one the device uses; a part in
+// memory the device cannot reach rejects the call before anything is enqueued.
+bool resolve_for_device(const e0_stack &in, e0_stack &out) {
+    out = in;
+    for (int i = 0; i < 9; ++i) {
+        hipPointerAttribute_t at{};
+        if (hipPointerGetAttributes(&at, in.part[i].ptr) != hipSuccess) {
+            (void)hipGetLastError();  // leave no error for the next launch check
+            return false;
+        }
+        if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) continue;
+        if (at.type != hipMemoryTypeHost || !at.devicePointer) return false;
+        out.part[i].ptr = at.devicePointer;
+    }
+    return true;
+}
+
 }  // namespace
 
 size_t e0_slot_workspace_bytes(const e0_moe_dims *dims, int32_t L, int32_t B, int32_t S) {
@@ -254,6 +273,8 @@ extern "C" e0_status e0_slot_update(const e0_moe_dims *dims, int32_t L, int32_t 
     const SlotLayout lay = slot_layout(L, B * K, S, E);
     E0_REQUIRE(ws && ws_bytes >= lay.total && (reinterpret_cast<uintptr_t>(ws) & 255) == 0, E0_ERR_CAPACITY);
     if (L == 0) return E0_OK;
+    e0_stack dstore;
+    E0_REQUIRE(resolve_for_device(*store, dstore), E0_ERR_INVALID_ARG);
 
     CopyArgs c{};
     const int64_t qb = (int64_t)d * f / 2, sb = (int64_t)d * f / kGroup * 2;
@@ -279,9 +300,9 @@ extern "C" e0_status e0_slot_update(const e0_moe_dims *dims, int32_t L, int32_t 
     c.ncopy = a.ncopy;
     c.copy_slot = a.copy_slot;
     c.copy_exp = a.copy_exp;
-    c.store = to_stack(*store);
+    c.store = to_stack(dstore);
     c.pool = to_stack(*pool);
-    c.contiguous = stack_contiguous(store, c.part_end) && stack_contiguous(pool, c.part_end);
+    c.contiguous = stack_contiguous(&dstore, c.part_end) && stack_contiguous(pool, c.part_end);
     hipLaunchKernelGGL(slot_copy_kernel, dim3(L, lay.maxc, (unsigned)chunks), dim3(kThreads), 0, st, c);
     return e0_launch_status();
 }
