@@ -19,7 +19,7 @@
 //  3. gemm2    (tiles x d_model/256): Yb[pair] = w_pair * (H D^T).
 //  4. combine  : y[t] = sum over k in order of Yb[t*K + k].
 // The last M-tile of an expert runs only the 32-row MFMA blocks that hold
-// rows. Work items are dealt to the eight XCDs in contiguous ranges.
+// rows. Tiles are dealt to the eight XCDs round robin, heaviest first.
 //
 // MFMA v_mfma_f32_32x32x16_f16 on fp16 operands. A rows go from global memory
 // straight into LDS; B fragments are code words dequantised in registers (one
@@ -34,6 +34,7 @@ constexpr int kTM = 128;         // rows per M-tile
 constexpr int kGemmThreads = 256;
 constexpr int kSortThreads = 1024;
 constexpr int kMaxSortE = 1024;
+constexpr int kSortBatch = 8;    // pairs per thread whose loads are issued together
 constexpr int kStepK = 128;      // reduction inputs per pipeline step (two groups)
 constexpr int kARow = kStepK;    // halves per LDS row of A (XOR-swizzled chunks, no padding)
 
@@ -83,57 +84,99 @@ E0_DEV int block_scan_1024(int v, int *lds16, int &total) {
     return base + inc - v;
 }
 
+// Cost class of an M-tile holding r rows: the GEMM runs 4, 2 or 1 blocks of
+// 32 rows for it.
+E0_DEV int tile_class(int r) { return r > 64 ? 0 : r > 32 ? 1 : 2; }
+
 __global__ __launch_bounds__(kSortThreads) void prefill_sort_kernel(PrefillArgs a) {
     __shared__ int s_cnt[kMaxSortE];
     __shared__ int s_fill[kMaxSortE];
     __shared__ int s_scan[kSortThreads / 64];
     const int tid = threadIdx.x;
     const int E = a.E, n = a.n;
-    for (int e = tid; e < E; e += kSortThreads) s_cnt[e] = s_fill[e] = 0;
+    for (int e = tid; e < E; e += kSortThreads) s_cnt[e] = 0;
     __syncthreads();
-    // Counts per expert (LDS atomics; the counts do not depend on their order).
-    for (int p = tid; p < n; p += kSortThreads) {
-        const int e = a.idx[p];
-        if (e >= 0 && e < E)
-            atomicAdd(&s_cnt[e], 1);
-        else
-            set_err(a.err, E0_DEV_BAD_ID);
+    // Counts per expert (LDS atomics; the counts do not depend on their
+    // order). A batch of ids is loaded before the first atomic of the batch,
+    // so the global loads overlap instead of waiting one by one.
+    for (int base = 0; base < n; base += kSortThreads * kSortBatch) {
+        int ids[kSortBatch];
+#pragma unroll
+        for (int i = 0; i < kSortBatch; ++i) {
+            const int p = base + i * kSortThreads + tid;
+            ids[i] = p < n ? a.idx[p] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < kSortBatch; ++i) {
+            if (base + i * kSortThreads + tid >= n) continue;
+            const int e = ids[i];
+            if (e >= 0 && e < E)
+                atomicAdd(&s_cnt[e], 1);
+            else
+                set_err(a.err, E0_DEV_BAD_ID);
+        }
     }
     __syncthreads();
-    // Exclusive scan -> first sorted row of each expert; tiles per expert.
+    // Exclusive scans: first sorted row of each expert, and the position of
+    // each of its M-tiles in the tile list. The list holds the tiles by cost
+    // class (128-row tiles and tails above 64 rows, then tails of 33..64
+    // rows, then tails of at most 32), each class in expert order.
     const int eper = (E + kSortThreads - 1) / kSortThreads;
-    int local = 0, nt = 0;
+    int rows = 0, nc[3] = {0, 0, 0};
     for (int e = tid * eper; e < (tid + 1) * eper && e < E; ++e) {
-        local += s_cnt[e];
-        nt += (s_cnt[e] + kTM - 1) / kTM;
+        const int c = s_cnt[e];
+        rows += c;
+        nc[0] += c / kTM;
+        if (c % kTM) ++nc[tile_class(c % kTM)];
     }
-    int total, tt;
-    int run = block_scan_1024(local, s_scan, total);
-    int tb = block_scan_1024(nt, s_scan, tt);
+    int total, tot[3], pos[3];
+    int run = block_scan_1024(rows, s_scan, total);
+    for (int k = 0; k < 3; ++k) pos[k] = block_scan_1024(nc[k], s_scan, tot[k]);
+    pos[1] += tot[0];
+    pos[2] += tot[0] + tot[1];
     for (int e = tid * eper; e < (tid + 1) * eper && e < E; ++e) {
+        const int c = s_cnt[e];
         a.off[e] = run;
         s_fill[e] = run;
-        for (int m = 0; m < s_cnt[e]; m += kTM, ++tb) {
-            a.tile_e[tb] = e;
-            a.tile_m0[tb] = run + m;
+        int m = 0;
+        for (; m + kTM <= c; m += kTM, ++pos[0]) {
+            a.tile_e[pos[0]] = e;
+            a.tile_m0[pos[0]] = run + m;
         }
-        run += s_cnt[e];
+        if (m < c) {
+            const int k = tile_class(c - m);
+            a.tile_e[pos[k]] = e;
+            a.tile_m0[pos[k]] = run + m;
+            ++pos[k];
+        }
+        run += c;
     }
     if (tid == 0) {
         a.off[E] = total;
-        a.ntiles[0] = tt;
+        a.ntiles[0] = tot[0] + tot[1] + tot[2];
     }
     __syncthreads();
-    // Scatter. The order of rows inside an expert's block follows the LDS
-    // atomics and may differ from run to run; no output depends on it (every
-    // GEMM row is computed on its own and results are stored by pair index).
-    for (int p = tid; p < n; p += kSortThreads) {
-        const int e = a.idx[p];
-        const float wp = a.w[p];
-        if (e >= 0 && e < E) {
-            const int row = atomicAdd(&s_fill[e], 1);
-            a.perm[row] = p;
-            a.wsort[row] = wp;
+    // Scatter, ids and weights of a batch loaded first. The order of rows
+    // inside an expert's block follows the LDS atomics and may differ from
+    // run to run; no output depends on it (every GEMM row is computed on its
+    // own and results are stored by pair index).
+    for (int base = 0; base < n; base += kSortThreads * kSortBatch) {
+        int ids[kSortBatch];
+        float wts[kSortBatch];
+#pragma unroll
+        for (int i = 0; i < kSortBatch; ++i) {
+            const int p = base + i * kSortThreads + tid;
+            ids[i] = p < n ? a.idx[p] : -1;
+            wts[i] = p < n ? a.w[p] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < kSortBatch; ++i) {
+            const int e = ids[i];
+            if (e >= 0 && e < E) {
+                const int row = atomicAdd(&s_fill[e], 1);
+                a.perm[row] = base + i * kSortThreads + tid;
+                a.wsort[row] = wts[i];
+            }
         }
     }
 }
@@ -379,17 +422,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void prefill_gemm_kernel(PrefillAr
     constexpr int kCols = 4 * 32 * (GATEUP ? 1 : NB);
     __shared__ __attribute__((aligned(16))) uint16_t s_a[2][kTM * kARow];
     const int nN = (GATEUP ? a.f : a.d) / kCols;
-    // Work items in tile-major order (the column blocks of one M-tile, then
-    // the next tile of the same expert) cut into eight contiguous ranges, one
-    // per XCD (the hardware deals block b to XCD b % 8), so rows of x and
-    // weight slices are re-read from the XCD's own L2.
-    const int nwork = a.ntiles[0] * nN;
-    const int per = (nwork + 7) >> 3;
+    // The hardware deals block b to XCD b % 8 and dispatches in block order.
+    // Tile j of the list (heaviest class first) goes to XCD j % 8, and its
+    // column blocks take consecutive places on that XCD: the heavy tiles are
+    // spread over all XCDs (and their CUs) before any light one starts, and
+    // the column blocks of one tile re-read its rows from the same L2.
     const int bi = blockIdx.x >> 3;
-    if (bi >= per) return;
-    const int wi = (blockIdx.x & 7) * per + bi;
-    if (wi >= nwork) return;
-    const int tile = wi / nN, nt = wi % nN;
+    const int tile = (bi / nN) * 8 + (blockIdx.x & 7), nt = bi % nN;
+    if (tile >= a.ntiles[0]) return;
     const int e = a.tile_e[tile], m0 = a.tile_m0[tile];
     const int m_end = a.off[e + 1];
     const int rows = m_end - m0;
@@ -515,7 +555,7 @@ extern "C" e0_status e0_moe_sorted_prefill(const e0_moe_dims *dims, int32_t T, c
     if ((s = e0_launch_status())) return s;
     // Grids cover the largest tile count in whole groups of eight blocks;
     // blocks past the tiles the sort produced exit at once.
-    auto grid = [&](int cols) { return dim3((unsigned)((((int64_t)lay.max_tiles * (cols) + 7) / 8) * 8)); };
+    auto grid = [&](int cols) { return dim3((unsigned)(((int64_t)lay.max_tiles + 7) / 8 * (cols) * 8)); };
     hipLaunchKernelGGL((prefill_gemm_kernel<2, true>), grid(f / 128), dim3(kGemmThreads), 0, st, a);
     if ((s = e0_launch_status())) return s;
     if (d % 256 == 0)
