@@ -63,48 +63,71 @@ struct PrefillArgs {
 // ---------------------------------------------------------------------------
 // 1. sort (one workgroup)
 // ---------------------------------------------------------------------------
-E0_DEV int block_scan_1024(int v, int *lds16, int &total) {
+// Exclusive scan of four ints per thread over the workgroup, all four in one
+// pass (one pair of barriers).
+E0_DEV void block_scan4_1024(const int (&v)[4], int (&ex)[4], int (&total)[4], int (*lds)[4]) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int inc = v;
+    int inc[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(inc, o);
-        if (lane >= o) inc += t;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int t = __shfl_up(inc[k], o);
+            if (lane >= o) inc[k] += t;
+        }
     }
-    if (lane == 63) lds16[wv] = inc;
+    if (lane == 63)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) lds[wv][k] = inc[k];
     __syncthreads();
-    int base = 0;
-    total = 0;
-    for (int i = 0; i < kSortThreads / 64; ++i) {
-        const int t = lds16[i];
-        if (i < wv) base += t;
-        total += t;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        int base = 0, tot = 0;
+        for (int i = 0; i < kSortThreads / 64; ++i) {
+            const int t = lds[i][k];
+            if (i < wv) base += t;
+            tot += t;
+        }
+        ex[k] = base + inc[k] - v[k];
+        total[k] = tot;
     }
     __syncthreads();
-    return base + inc - v;
 }
 
 // Cost class of an M-tile holding r rows: the GEMM runs 4, 2 or 1 blocks of
 // 32 rows for it.
 E0_DEV int tile_class(int r) { return r > 64 ? 0 : r > 32 ? 1 : 2; }
 
+// One workgroup. Every global store comes after the last barrier: a barrier
+// also waits for the workgroup's outstanding stores, so stores issued before
+// one would be waited for there.
 __global__ __launch_bounds__(kSortThreads) void prefill_sort_kernel(PrefillArgs a) {
     __shared__ int s_cnt[kMaxSortE];
     __shared__ int s_fill[kMaxSortE];
-    __shared__ int s_scan[kSortThreads / 64];
+    __shared__ int s_scan[kSortThreads / 64][4];
     const int tid = threadIdx.x;
     const int E = a.E, n = a.n;
+    // The ids and weights of the first batch of pairs are loaded first and
+    // stay in registers; each later batch is loaded whole before its atomics,
+    // so the global loads overlap instead of waiting one by one.
+    int ids0[kSortBatch];
+    float wts0[kSortBatch];
+#pragma unroll
+    for (int i = 0; i < kSortBatch; ++i) {
+        const int p = i * kSortThreads + tid;
+        ids0[i] = p < n ? a.idx[p] : -1;
+        wts0[i] = p < n ? a.w[p] : 0.0f;
+    }
     for (int e = tid; e < E; e += kSortThreads) s_cnt[e] = 0;
     __syncthreads();
-    // Counts per expert (LDS atomics; the counts do not depend on their
-    // order). A batch of ids is loaded before the first atomic of the batch,
-    // so the global loads overlap instead of waiting one by one.
+    // Counts per expert (LDS atomics; the counts do not depend on their order).
+    int bad = 0;
     for (int base = 0; base < n; base += kSortThreads * kSortBatch) {
         int ids[kSortBatch];
 #pragma unroll
         for (int i = 0; i < kSortBatch; ++i) {
             const int p = base + i * kSortThreads + tid;
-            ids[i] = p < n ? a.idx[p] : 0;
+            ids[i] = base == 0 ? ids0[i] : p < n ? a.idx[p] : 0;
         }
 #pragma unroll
         for (int i = 0; i < kSortBatch; ++i) {
@@ -113,7 +136,7 @@ __global__ __launch_bounds__(kSortThreads) void prefill_sort_kernel(PrefillArgs 
             if (e >= 0 && e < E)
                 atomicAdd(&s_cnt[e], 1);
             else
-                set_err(a.err, E0_DEV_BAD_ID);
+                bad = 1;
         }
     }
     __syncthreads();
@@ -122,52 +145,32 @@ __global__ __launch_bounds__(kSortThreads) void prefill_sort_kernel(PrefillArgs 
     // class (128-row tiles and tails above 64 rows, then tails of 33..64
     // rows, then tails of at most 32), each class in expert order.
     const int eper = (E + kSortThreads - 1) / kSortThreads;
-    int rows = 0, nc[3] = {0, 0, 0};
+    int cnt4[4] = {0, 0, 0, 0};  // rows, tiles of class 0, 1, 2
     for (int e = tid * eper; e < (tid + 1) * eper && e < E; ++e) {
         const int c = s_cnt[e];
-        rows += c;
-        nc[0] += c / kTM;
-        if (c % kTM) ++nc[tile_class(c % kTM)];
+        cnt4[0] += c;
+        cnt4[1] += c / kTM;
+        if (c % kTM) ++cnt4[1 + tile_class(c % kTM)];
     }
-    int total, tot[3], pos[3];
-    int run = block_scan_1024(rows, s_scan, total);
-    for (int k = 0; k < 3; ++k) pos[k] = block_scan_1024(nc[k], s_scan, tot[k]);
-    pos[1] += tot[0];
-    pos[2] += tot[0] + tot[1];
+    int ex[4], tot[4];
+    block_scan4_1024(cnt4, ex, tot, s_scan);
+    int run = ex[0];
     for (int e = tid * eper; e < (tid + 1) * eper && e < E; ++e) {
-        const int c = s_cnt[e];
-        a.off[e] = run;
         s_fill[e] = run;
-        int m = 0;
-        for (; m + kTM <= c; m += kTM, ++pos[0]) {
-            a.tile_e[pos[0]] = e;
-            a.tile_m0[pos[0]] = run + m;
-        }
-        if (m < c) {
-            const int k = tile_class(c - m);
-            a.tile_e[pos[k]] = e;
-            a.tile_m0[pos[k]] = run + m;
-            ++pos[k];
-        }
-        run += c;
-    }
-    if (tid == 0) {
-        a.off[E] = total;
-        a.ntiles[0] = tot[0] + tot[1] + tot[2];
+        run += s_cnt[e];
     }
     __syncthreads();
-    // Scatter, ids and weights of a batch loaded first. The order of rows
-    // inside an expert's block follows the LDS atomics and may differ from
-    // run to run; no output depends on it (every GEMM row is computed on its
-    // own and results are stored by pair index).
+    // Scatter. The order of rows inside an expert's block follows the LDS
+    // atomics and may differ from run to run; no output depends on it (every
+    // GEMM row is computed on its own and results are stored by pair index).
     for (int base = 0; base < n; base += kSortThreads * kSortBatch) {
         int ids[kSortBatch];
         float wts[kSortBatch];
 #pragma unroll
         for (int i = 0; i < kSortBatch; ++i) {
             const int p = base + i * kSortThreads + tid;
-            ids[i] = p < n ? a.idx[p] : -1;
-            wts[i] = p < n ? a.w[p] : 0.0f;
+            ids[i] = base == 0 ? ids0[i] : p < n ? a.idx[p] : -1;
+            wts[i] = base == 0 ? wts0[i] : p < n ? a.w[p] : 0.0f;
         }
 #pragma unroll
         for (int i = 0; i < kSortBatch; ++i) {
@@ -178,6 +181,30 @@ __global__ __launch_bounds__(kSortThreads) void prefill_sort_kernel(PrefillArgs 
                 a.wsort[row] = wts[i];
             }
         }
+    }
+    // Expert offsets and the tile list.
+    int pos[3] = {ex[1], tot[1] + ex[2], tot[1] + tot[2] + ex[3]};
+    run = ex[0];
+    for (int e = tid * eper; e < (tid + 1) * eper && e < E; ++e) {
+        const int c = s_cnt[e];
+        a.off[e] = run;
+        int m = 0;
+        for (; m + kTM <= c; m += kTM, ++pos[0]) {
+            a.tile_e[pos[0]] = e;
+            a.tile_m0[pos[0]] = run + m;
+        }
+        if (m < c) {
+            const int k = tile_class(c - m);
+            const int q = k == 0 ? pos[0]++ : k == 1 ? pos[1]++ : pos[2]++;
+            a.tile_e[q] = e;
+            a.tile_m0[q] = run + m;
+        }
+        run += c;
+    }
+    if (bad) set_err(a.err, E0_DEV_BAD_ID);
+    if (tid == 0) {
+        a.off[E] = tot[0];
+        a.ntiles[0] = tot[1] + tot[2] + tot[3];
     }
 }
 
