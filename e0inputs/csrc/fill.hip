@@ -99,9 +99,11 @@ extern "C" int e0gen_fill_experts(void *dst, int64_t stride, const uint64_t *key
         a.ngrp[m] = (m < 2 ? d : f) / 64;
     }
     if (stride < acc * 16 || (stride & 15) || (reinterpret_cast<uintptr_t>(dst) & 15)) return 1;
+    (void)hipGetLastError();  // a status left pending by the caller's earlier runtime calls
     if (n_experts == 0) return 0;
     if (n_experts > 65535) return 1;
     hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((acc + 255) / 256), n_experts), dim3(256), 0,
                        static_cast<hipStream_t>(stream), a);
-    return hipGetLastError() == hipSuccess ? 0 : 2;
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? 0 : 1000 + (int)e;  // 1000 + the HIP error code
 }

@@ -36,6 +36,7 @@ def lib():
     if _LIB is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} not built")
+        import torch  # noqa: F401  (bind to torch's HIP runtime, as in the libe0 binding)
         _LIB = C.CDLL(LIB_PATH)
         _LIB.e0gen_fill_experts.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_int, C.c_int, C.c_int,
                                             C.c_void_p]
@@ -61,6 +62,6 @@ def fill_experts(dst_ptr: int, stride: int, seed: int, layer: int, experts, d: i
     rc = lib().e0gen_fill_experts(C.c_void_p(dst_ptr), stride, C.c_void_p(keys.data_ptr()), len(experts), d, f,
                                   C.c_void_p(st))
     if rc:
-        raise RuntimeError(f"e0gen_fill_experts failed ({rc})")
+        raise RuntimeError(f"e0gen_fill_experts failed ({rc}" + (f": HIP error {rc - 1000}" if rc >= 1000 else "") + ")")
     torch.cuda.synchronize()  # keys must outlive the fill; this is set-up, not a timed path
     del keys

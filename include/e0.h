@@ -54,7 +54,8 @@ enum {
     E0_ERR_INVALID_ARG = 1,       /* null pointer, negative size, bad mode */
     E0_ERR_UNSUPPORTED_SHAPE = 2, /* d or f not a multiple of 64, K > E, groups that do not divide E, ... */
     E0_ERR_CAPACITY = 3,          /* workspace too small, S too small, size over a kernel limit */
-    E0_ERR_HIP = 4                /* a HIP launch failed (hipGetLastError) */
+    E0_ERR_HIP = 4                /* a HIP launch of this call failed (hipGetLastError; a status left
+                                     pending by the caller's earlier runtime calls is cleared on entry) */
 };
 
 /* Bits of the device error word. */

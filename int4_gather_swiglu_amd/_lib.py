@@ -67,6 +67,11 @@ def lib() -> C.CDLL:
     if _LIB is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"libe0.so not built: run __graft_entry__.build() (expected {LIB_PATH})")
+        # torch first: its bundled HIP runtime has the same soname as the
+        # system one libe0.so was linked against, so loading torch first makes
+        # this library bind to torch's runtime instead of starting a second
+        # HIP runtime in the process (which then finds no device).
+        import torch  # noqa: F401
         L = C.CDLL(LIB_PATH)
         L.e0_abi_version.restype = C.c_int32
         L.e0_status_string.restype = C.c_char_p

@@ -1581,6 +1581,7 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
                                           const int32_t *idx, const float *w, const int32_t *slot_of, int32_t S,
                                           const e0_stack *pool, const e0_shared *shared, float *y, void *ws,
                                           size_t ws_bytes, int32_t *dev_err, void *stream) {
+    e0_clear_stale_error();
     E0_REQUIRE(dims && pool, E0_ERR_INVALID_ARG);
     const int d = dims->d_model, f = dims->d_ff, E = dims->n_experts, K = dims->top_k;
     E0_REQUIRE(L >= 0 && B >= 1 && S >= 1 && E >= 1 && K >= 1, E0_ERR_INVALID_ARG);
@@ -1742,6 +1743,7 @@ extern "C" e0_status e0_moe_chained_decode(const e0_moe_dims *dims, int32_t L, c
                                            float eps, const int32_t *idx, const float *w, const int32_t *slot_of,
                                            int32_t S, const e0_stack *pool, float *y, float *r_out, void *ws,
                                            size_t ws_bytes, int32_t *dev_err, void *stream) {
+    e0_clear_stale_error();
     E0_REQUIRE(dims && pool, E0_ERR_INVALID_ARG);
     const int d = dims->d_model, f = dims->d_ff, E = dims->n_experts, K = dims->top_k;
     E0_REQUIRE(L >= 0 && S >= 1 && E >= 1 && K >= 1 && K <= E && E <= kMaxE, E0_ERR_INVALID_ARG);

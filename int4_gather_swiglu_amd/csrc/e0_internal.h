@@ -183,6 +183,11 @@ uint64_t e0_next_epoch();
         if (!(cond)) return (code); \
     } while (0)
 
+// Every entry point starts with this: a status left pending in the calling
+// thread by an earlier runtime call (the caller's, not this library's) is
+// cleared, so that e0_launch_status reports this call's launches only.
+inline void e0_clear_stale_error() { (void)hipGetLastError(); }
+
 inline e0_status e0_launch_status() {
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? E0_OK : E0_ERR_HIP;

@@ -535,6 +535,7 @@ size_t e0_prefill_workspace_bytes(const e0_moe_dims *dims, int32_t T) {
 extern "C" e0_status e0_moe_sorted_prefill(const e0_moe_dims *dims, int32_t T, const uint16_t *x, const int32_t *idx,
                                            const float *w, const e0_stack *layer, float *y, void *ws, size_t ws_bytes,
                                            int32_t *dev_err, void *stream) {
+    e0_clear_stale_error();
     E0_REQUIRE(dims && layer, E0_ERR_INVALID_ARG);
     const int d = dims->d_model, f = dims->d_ff, E = dims->n_experts, K = dims->top_k;
     E0_REQUIRE(T >= 0 && E >= 1 && K >= 1, E0_ERR_INVALID_ARG);

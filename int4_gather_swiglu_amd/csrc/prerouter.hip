@@ -180,6 +180,7 @@ extern "C" e0_status e0_prerouter(const e0_prerouter_heads *heads, int32_t n_hea
                                   const uint16_t *h, const int32_t *cur_idx, const int32_t *prev_idx,
                                   const e0_route_params *p, int32_t *next_idx, float *next_w, float *logits_out,
                                   void *ws, size_t ws_bytes, void *stream) {
+    e0_clear_stale_error();
     e0_status s = e0_route_validate(p, E);
     if (s) return s;
     E0_REQUIRE(heads, E0_ERR_INVALID_ARG);

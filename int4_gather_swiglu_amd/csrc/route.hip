@@ -15,7 +15,6 @@
 namespace {
 
 constexpr int kMaxE = 1024;
-constexpr int kPerLane = kMaxE / kWave;  // 16
 constexpr int kRouteWaves = 4;
 
 struct RouteArgs {
@@ -50,6 +49,8 @@ E0_DEV void wave_argmax(float &v, int &e) {
 
 E0_DEV float sigm(float l) { return 1.0f / (1.0f + expf(-l)); }
 
+// PL = logits per lane (E <= 64 PL): the loops below run over PL entries only.
+template <int PL>
 __global__ __launch_bounds__(kWave *kRouteWaves) void route_select_kernel(RouteArgs a) {
     __shared__ float lds_l[kRouteWaves][kMaxE];
     __shared__ float lds_gs[kRouteWaves][kWave];
@@ -59,10 +60,10 @@ __global__ __launch_bounds__(kWave *kRouteWaves) void route_select_kernel(RouteA
     if (row >= a.rows) return;
     const int E = a.E, K = a.K;
 
-    float l[kPerLane];
-    bool avail[kPerLane];
+    float l[PL];
+    bool avail[PL];
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
+    for (int i = 0; i < PL; ++i) {
         const int e = lane + kWave * i;
         avail[i] = false;
         l[i] = -INFINITY;
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(kWave *kRouteWaves) void route_select_kernel(RouteA
         // Group scores: sum of the two largest sigmoid scores per contiguous group.
         const int per = E / a.n_groups;
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
+        for (int i = 0; i < PL; ++i) {
             const int e = lane + kWave * i;
             if (e < E) lds_l[wv][e] = l[i];
         }
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(kWave *kRouteWaves) void route_select_kernel(RouteA
         lds_gs[wv][lane] = kept ? 1.0f : 0.0f;
         wave_lds_sync();
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
+        for (int i = 0; i < PL; ++i) {
             const int e = lane + kWave * i;
             if (e < E) avail[i] = lds_gs[wv][e / per] != 0.0f;
         }
@@ -126,11 +127,11 @@ __global__ __launch_bounds__(kWave *kRouteWaves) void route_select_kernel(RouteA
         float bv = -INFINITY;
         int be = -1;
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i)
+        for (int i = 0; i < PL; ++i)
             if (avail[i]) better(bv, be, l[i], lane + kWave * i);
         wave_argmax(bv, be);
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i)
+        for (int i = 0; i < PL; ++i)
             if (lane + kWave * i == be) avail[i] = false;
         if (lane == k) {
             my_e = be;
@@ -221,13 +222,24 @@ e0_status e0_route_select_launch(const e0_route_params *p, int rows, int E, cons
     RouteArgs a{logits, fp16, rows, E, p->mode, p->k, p->n_groups, p->topk_groups, p->scale, p->eps, idx, w,
                 logits_out};
     const int blocks = (rows + kRouteWaves - 1) / kRouteWaves;
-    hipLaunchKernelGGL(route_select_kernel, dim3(blocks), dim3(kWave * kRouteWaves), 0, st, a);
+    const dim3 g(blocks), b(kWave * kRouteWaves);
+    if (E <= kWave)
+        hipLaunchKernelGGL(route_select_kernel<1>, g, b, 0, st, a);
+    else if (E <= 2 * kWave)
+        hipLaunchKernelGGL(route_select_kernel<2>, g, b, 0, st, a);
+    else if (E <= 4 * kWave)
+        hipLaunchKernelGGL(route_select_kernel<4>, g, b, 0, st, a);
+    else if (E <= 8 * kWave)
+        hipLaunchKernelGGL(route_select_kernel<8>, g, b, 0, st, a);
+    else
+        hipLaunchKernelGGL(route_select_kernel<kMaxE / kWave>, g, b, 0, st, a);
     return e0_launch_status();
 }
 
 extern "C" e0_status e0_route(const e0_route_params *p, int32_t n_layers, int32_t T, int32_t E, const void *logits,
                               int32_t logits_fp16, const uint16_t *x, const uint16_t *w_router, int32_t d,
                               int32_t *idx, float *w, float *logits_out, void *stream) {
+    e0_clear_stale_error();
     e0_status s = e0_route_validate(p, E);
     if (s) return s;
     E0_REQUIRE(n_layers >= 0 && T >= 0, E0_ERR_INVALID_ARG);

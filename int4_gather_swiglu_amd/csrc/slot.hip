@@ -263,6 +263,7 @@ extern "C" e0_status e0_slot_update(const e0_moe_dims *dims, int32_t L, int32_t 
                                     const int32_t *next_idx, const int32_t *cur_idx, int32_t *slot_of,
                                     int32_t *expert_of, const e0_stack *store, const e0_stack *pool,
                                     int32_t *n_copied, void *ws, size_t ws_bytes, int32_t *dev_err, void *stream) {
+    e0_clear_stale_error();
     E0_REQUIRE(dims && store && pool, E0_ERR_INVALID_ARG);
     const int d = dims->d_model, f = dims->d_ff, E = dims->n_experts, K = dims->top_k;
     E0_REQUIRE(L >= 0 && B >= 1 && S >= 1 && K >= 1 && E >= 1, E0_ERR_INVALID_ARG);
