@@ -28,6 +28,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace {
 
 constexpr int kTM = 128;         // rows per M-tile
@@ -253,7 +255,6 @@ E0_DEV void prefill_tile(const PrefillArgs &a, uint16_t (*s_a)[kTM * kARow], int
     constexpr int kCols = 4 * 32 * (GATEUP ? 1 : NB);  // output columns per workgroup
     constexpr int kMf = NMB * NB;                      // MFMAs per code word
     constexpr int kPairs = 4 * NB;                     // weight pairs per code word set
-    constexpr int kPpm = kPairs / kMf > 0 ? kPairs / kMf : 1;  // pairs dequantised per MFMA
     const int Nall = GATEUP ? a.f : a.d;
     const int Kdim = GATEUP ? a.d : a.f;
     const int ngroups = Kdim / kGroup;
@@ -343,45 +344,61 @@ E0_DEV void prefill_tile(const PrefillArgs &a, uint16_t (*s_a)[kTM * kARow], int
         const int c = (h * 8 + j) ^ (r & 15);
         return *reinterpret_cast<const h8 *>(&s_a[buf][r * kStepK + c * 8]);
     };
-    // Pair p (0 .. 4 NB - 1) of code word j: operand p / 4, byte p % 4.
-    auto dq_pair = [&](const Bst &b, int j, int p) {
-        const int n = p >> 2;
-        const f16 sv = __builtin_bit_cast(f16, (uint16_t)b.s[n]), bv = __builtin_bit_cast(f16, (uint16_t)b.b[n]);
-        return dequant_pair(b.q[n][j >> 2][j & 3], p & 3, f16x2{sv, sv}, f16x2{bv, bv}, km, kc);
+    // Pairs p0 .. p0 + N - 1 of code word j, dequantised stage by stage (all
+    // byte placements, then all masks, then both fmas of every pair), so the N
+    // dependency chains overlap instead of running one after another.
+    auto dq_pairs = [&](const Bst &b, int j, int p0, auto &dst, auto cnt) {
+        constexpr int N = decltype(cnt)::value;
+        uint32_t t[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int p = p0 + i;
+            t[i] = __builtin_amdgcn_perm(b.q[p >> 2][j >> 2][j & 3], b.q[p >> 2][j >> 2][j & 3],
+                                         0x0c000c00u | (uint32_t)(p & 3) << 16 | (uint32_t)(p & 3));
+        }
+#pragma unroll
+        for (int i = 0; i < N; ++i) t[i] = and_or_v(t[i], km, kc);
+        const f16x2 kmul = f16x2{(f16)1.0f, (f16)0.0625f};
+        const f16x2 kadd = f16x2{(f16)-1024.0f, (f16)-64.0f};
+        f16x2 q[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) q[i] = __builtin_elementwise_fma(as_h2(t[i]), kmul, kadd);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int p = p0 + i, n = p >> 2;
+            const f16 sv = __builtin_bit_cast(f16, (uint16_t)b.s[n]), bv = __builtin_bit_cast(f16, (uint16_t)b.b[n]);
+            const f16x2 v = __builtin_elementwise_fma(q[i], f16x2{sv, sv}, f16x2{bv, bv});
+            dst[n][2 * (p & 3)] = v[0];
+            dst[n][2 * (p & 3) + 1] = v[1];
+        }
     };
+    // MFMAs in windows of two; each window also dequantises its share of the
+    // next code word (kPairs / (kMf / 2) pairs) and reads the next A
+    // fragments, with a scheduling barrier between windows.
+    constexpr int kWin = kMf >= 2 ? 2 : 1;
+    constexpr int kPpw = kPairs / (kMf / kWin);
     auto compute = [&](int buf, const Bst &b) {
         h8 bcur[NB], af[NMB];
-#pragma unroll
-        for (int p = 0; p < kPairs; ++p) {
-            const f16x2 v = dq_pair(b, 0, p);
-            bcur[p >> 2][2 * (p & 3)] = v[0];
-            bcur[p >> 2][2 * (p & 3) + 1] = v[1];
-        }
+        dq_pairs(b, 0, 0, bcur, std::integral_constant<int, kPairs>{});
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) af[mb] = afrag(buf, mb, 0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             h8 bnx[NB], afn[NMB];
 #pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) {
+            for (int w0 = 0; w0 < kMf; w0 += kWin) {
 #pragma unroll
-                for (int n = 0; n < NB; ++n) {
+                for (int k = w0; k < w0 + kWin; ++k) {
+                    const int mb = k / NB, n = k % NB;
                     acc[n][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mb], bcur[n], acc[n][mb], 0, 0, 0);
-                    if (j < 7) {
-                        const int k = mb * NB + n;
-#pragma unroll
-                        for (int q = 0; q < kPpm; ++q) {
-                            const int p = k * kPpm + q;
-                            if (p < kPairs) {
-                                const f16x2 v = dq_pair(b, j + 1, p);
-                                bnx[p >> 2][2 * (p & 3)] = v[0];
-                                bnx[p >> 2][2 * (p & 3) + 1] = v[1];
-                            }
-                        }
-                        if (n == 0) afn[mb] = afrag(buf, mb, j + 1);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
                 }
+                if (j < 7) {
+                    dq_pairs(b, j + 1, (w0 / kWin) * kPpw, bnx, std::integral_constant<int, kPpw>{});
+#pragma unroll
+                    for (int k = w0; k < w0 + kWin; ++k)
+                        if (k % NB == 0) afn[k / NB] = afrag(buf, k / NB, j + 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
             if (j < 7) {
 #pragma unroll
