@@ -47,6 +47,7 @@ constexpr int kMaxK = 32;
 constexpr int kMaxE = 1024;
 constexpr int kMaxR = 32;
 constexpr int kDownRows = 64;  // output rows per down workgroup
+constexpr int kHChunkFloats = 8192;  // h floats staged in LDS per chunk of pairs (batched down)
 
 struct DecodeArgs {
     int L, B, K, E, S, d, f;
@@ -72,6 +73,7 @@ struct DecodeArgs {
     int32_t *uslot;  // [L][umax]
     int32_t *uoff;   // [L][umax + 1]
     int32_t *pairs;  // [L][B*K]
+    int32_t *pslot;  // [L][B*K] slot of the expert of each sorted pair (-1: not resident)
     float *hbuf;     // [L][B*K + B][f]
     float *lora_a;   // [L][B][3][r]
     uint32_t *hblk;  // [L][units][d_ff / 32][kBlk] (single-launch batch-1 path)
@@ -134,6 +136,7 @@ __global__ __launch_bounds__(kThreads) void decode_prep_kernel(DecodeArgs a) {
     __shared__ int s_cnt[kMaxE];
     __shared__ int s_base[kMaxE];
     __shared__ int s_ids[kMaxB * kMaxK];
+    __shared__ int s_slot[kMaxE];
     __shared__ int s_scan[kWaves];
     const int l = blockIdx.x;
     const int tid = threadIdx.x;
@@ -178,6 +181,7 @@ __global__ __launch_bounds__(kThreads) void decode_prep_kernel(DecodeArgs a) {
                     s = -1;
                 }
                 uslot[ubase] = s;
+                s_slot[e] = s;
                 ++ubase;
                 pbase += s_cnt[e];
             }
@@ -195,6 +199,7 @@ __global__ __launch_bounds__(kThreads) void decode_prep_kernel(DecodeArgs a) {
             int rank = 0;
             for (int q = 0; q < p; ++q) rank += s_ids[q] == e;
             pairs[s_base[e] + rank] = p;
+            a.pslot[(int64_t)l * n + s_base[e] + rank] = s_slot[e];
         }
     }
 
@@ -551,6 +556,10 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(DecodeArgs a) {
     constexpr int IT = DownCfg<LPR>::IT;
     __shared__ float s_acc[kMaxB][kDownRows];
     __shared__ float s_lora[kMaxB][kMaxR];
+    __shared__ __attribute__((aligned(16))) float s_h[kHChunkFloats];  // staged h rows (B > 1)
+    __shared__ int s_pid[kHChunkFloats / 128 + 1], s_pslot[kHChunkFloats / 128 + 1];
+    __shared__ float s_pw[kHChunkFloats / 128 + 1];
+    __shared__ __attribute__((aligned(16))) float s_hs[kHChunkFloats / 8];  // partial h sums (B > 1)
     const int lane = threadIdx.x & 63, wv = wave_id();
     const int gl = lane % LPR, grp = lane / LPR;
     const int l = blockIdx.x;
@@ -634,8 +643,12 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(DecodeArgs a) {
         return;
     }
 
-    // B > 1: unique experts in ascending id, each pair's contribution folded
-    // into the block's per-token accumulators in that order.
+    // B > 1: the layer's pairs in sorted order (unique experts ascending, an
+    // expert's pairs in token order), each pair's contribution folded into the
+    // block's per-token accumulators in that order. The h rows of a chunk of
+    // pairs are staged in LDS by one cooperative load (their latencies
+    // overlap), and the weight rows of the next pair are requested before the
+    // current pair is computed.
     for (int i = threadIdx.x; i < a.B * kDownRows; i += kThreads) s_acc[i / kDownRows][i % kDownRows] = 0.0f;
     __syncthreads();
     const int nu = a.ucnt[l];
@@ -649,16 +662,104 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(DecodeArgs a) {
             if (gl == 0 && row < d) s_acc[t][row - row0] += v;
         }
     };
-    for (int u = 0; u < nu; ++u) {
-        const int slot = a.uslot[(int64_t)l * a.umax + u];
-        if (slot < 0) continue;
-        for (int pi = uoff[u]; pi < uoff[u + 1]; ++pi) {
-            const int p = plist[pi];
-            float part[IT];
+    struct Wrows {
+        u32x4 q[IT];
+        float s[IT], b[IT];
+    };
+    auto load_w = [&](int slot, Wrows &wr) {
+        const rsrc_t qb = make_rsrc(part_at(a.pool.p[6], l, slot), (uint32_t)d * f / 2);
+        const rsrc_t sb = make_rsrc(part_at(a.pool.p[7], l, slot), (uint32_t)d * fgrp * 2);
+        const rsrc_t bb = make_rsrc(part_at(a.pool.p[8], l, slot), (uint32_t)d * fgrp * 2);
 #pragma unroll
-            for (int it = 0; it < IT; ++it) part[it] = 0.0f;
-            expert_rows(a.pool, slot, p, a.w[(int64_t)l * a.B * a.K + p], part);
-            fold(part, p / a.K);
+        for (int it = 0; it < IT; ++it) {
+            const uint32_t row = (uint32_t)min(rows[it], d - 1);  // clamped: in-bounds, never written
+            wr.q[it] = ld128(qb, row * (f / 2) + gl * 16);
+            wr.s[it] = h2f(ld16(sb, sb_index(row, (uint32_t)g, (uint32_t)fgrp) * 2));
+            wr.b[it] = h2f(ld16(bb, sb_index(row, (uint32_t)g, (uint32_t)fgrp) * 2));
+        }
+    };
+    const int npairs = nu > 0 ? cload(uoff, nu) : 0;
+    const int chunk = kHChunkFloats / f;  // pairs per LDS chunk (f <= 2048: at least 4)
+    const int32_t *pslot = a.pslot + (int64_t)l * a.B * a.K;
+    const float *wl = a.w + (int64_t)l * a.B * a.K;
+    Wrows wc, wn;
+    if (npairs > 0) {
+        const int s0 = cload(pslot, 0);
+        load_w(s0 < 0 ? 0 : s0, wc);
+    }
+    for (int c0 = 0; c0 < npairs; c0 += chunk) {
+        const int cn = min(chunk, npairs - c0);
+        __syncthreads();  // the previous chunk's LDS reads are done
+        // Per pair of the chunk: pair index, slot and routing weight (plus the
+        // slot of the first pair after the chunk); h rows in the layout
+        // [pair][i][gl] of 16-byte chunks, lane gl's i-th chunk of its 32
+        // columns, so the lanes of a row read consecutive chunks.
+        if (threadIdx.x <= cn && c0 + threadIdx.x < npairs) {
+            const int pi = c0 + threadIdx.x;
+            s_pslot[threadIdx.x] = pslot[pi];
+            if ((int)threadIdx.x < cn) {
+                const int p = plist[pi];
+                s_pid[threadIdx.x] = p;
+                s_pw[threadIdx.x] = wl[p];
+            }
+        }
+        // h of the chunk's pairs in the form dot_word_m2 takes: per lane group
+        // gl (32 columns) and word wd (8 columns), 4 dwords of fp16 hi pairs
+        // (element j with j + 4, odd j scaled by 1/16) and 4 of lo pairs
+        // (the rounding remainders), at [pair][2 wd + part][gl]; and the four
+        // partial sums of the group's h at [pair][gl][wd].
+        uint32_t *s_hq = reinterpret_cast<uint32_t *>(s_h);
+        for (int v = threadIdx.x; v < cn * LPR * 4; v += kThreads) {
+            const int pc = v / (LPR * 4), gq = (v / 4) % LPR, wd = v % 4;
+            const float *src = hrow(a, l, plist[c0 + pc]) + gq * 32 + wd * 8;
+            const f32x4 lo4 = *reinterpret_cast<const f32x4 *>(src), hi4 = *reinterpret_cast<const f32x4 *>(src + 4);
+            u32x4 qh, ql;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float sc = (j & 1) ? 0.0625f : 1.0f;
+                const float va = lo4[j] * sc, vb = hi4[j] * sc;
+                const f16 ha = (f16)va, hb = (f16)vb;
+                const f16 la = (f16)(va - (float)ha), lb = (f16)(vb - (float)hb);
+                qh[j] = (uint32_t)__builtin_bit_cast(uint16_t, ha) | (uint32_t)__builtin_bit_cast(uint16_t, hb) << 16;
+                ql[j] = (uint32_t)__builtin_bit_cast(uint16_t, la) | (uint32_t)__builtin_bit_cast(uint16_t, lb) << 16;
+            }
+            *reinterpret_cast<u32x4 *>(&s_hq[((pc * 8 + 2 * wd) * LPR + gq) * 4]) = qh;
+            *reinterpret_cast<u32x4 *>(&s_hq[((pc * 8 + 2 * wd + 1) * LPR + gq) * 4]) = ql;
+            s_hs[(pc * LPR + gq) * 4 + wd] = (lo4[0] + lo4[1]) + (lo4[2] + lo4[3]) + ((hi4[0] + hi4[1]) + (hi4[2] + hi4[3]));
+        }
+        __syncthreads();
+        for (int pc = 0; pc < cn; ++pc) {
+            const int pi = c0 + pc;
+            if (pi + 1 < npairs) {
+                const int sn = s_pslot[pc + 1];
+                load_w(sn < 0 ? 0 : sn, wn);
+            }
+            if (s_pslot[pc] >= 0) {
+                uint32_t hh[16], hl[16];
+#pragma unroll
+                for (int wd = 0; wd < 4; ++wd) {
+                    const u32x4 vh = *reinterpret_cast<const u32x4 *>(&s_hq[((pc * 8 + 2 * wd) * LPR + gl) * 4]);
+                    const u32x4 vl = *reinterpret_cast<const u32x4 *>(&s_hq[((pc * 8 + 2 * wd + 1) * LPR + gl) * 4]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        hh[4 * wd + j] = vh[j];
+                        hl[4 * wd + j] = vl[j];
+                    }
+                }
+                const f32x4 hs4 = *reinterpret_cast<const f32x4 *>(&s_hs[(pc * LPR + gl) * 4]);
+                const float hsum = (hs4[0] + hs4[1]) + (hs4[2] + hs4[3]);
+                const float wk = s_pw[pc];
+                float part[IT];
+#pragma unroll
+                for (int it = 0; it < IT; ++it) {
+                    float dacc = 0.0f;
+#pragma unroll
+                    for (int wd = 0; wd < 4; ++wd) dacc = dot_word_m2(wc.q[it][wd], hh + 4 * wd, hl + 4 * wd, dacc);
+                    part[it] = wk * ((wc.s[it] * kDenormScale) * dacc + wc.b[it] * hsum);
+                }
+                fold(part, s_pid[pc] / a.K);
+            }
+            wc = wn;
         }
     }
     if (a.has_shared) {
@@ -1448,7 +1549,7 @@ int d_lpr(int d, int &np) {
 int f_lpr(int f) { return (f >= 128 && f <= 2048 && pow2(f)) ? f / 32 : 0; }
 
 struct Layout {
-    size_t ucnt, uexp, uslot, uoff, pairs, hbuf, lora, flags, hblk, dflags, total;
+    size_t ucnt, uexp, uslot, uoff, pairs, pslot, hbuf, lora, flags, hblk, dflags, total;
 };
 
 // Output rows per wavefront of a down item of the single-launch kernel: at
@@ -1469,6 +1570,8 @@ Layout decode_layout(int L, int B, int K, int E, int f, int r, int n_dn = 0) {
     o.uoff = off;
     off = e0_align(off + sizeof(int32_t) * (size_t)L * (umax + 1));
     o.pairs = off;
+    off = e0_align(off + sizeof(int32_t) * (size_t)L * B * K);
+    o.pslot = off;
     off = e0_align(off + sizeof(int32_t) * (size_t)L * B * K);
     o.hbuf = off;
     off = e0_align(off + sizeof(float) * (size_t)L * (B * K + B) * f);
@@ -1648,6 +1751,7 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
     a.uslot = reinterpret_cast<int32_t *>(wsb + lay.uslot);
     a.uoff = reinterpret_cast<int32_t *>(wsb + lay.uoff);
     a.pairs = reinterpret_cast<int32_t *>(wsb + lay.pairs);
+    a.pslot = reinterpret_cast<int32_t *>(wsb + lay.pslot);
     a.hbuf = reinterpret_cast<float *>(wsb + lay.hbuf);
     a.lora_a = reinterpret_cast<float *>(wsb + lay.lora);
     a.flags = reinterpret_cast<uint64_t *>(wsb + lay.flags);
