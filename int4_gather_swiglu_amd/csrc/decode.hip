@@ -47,7 +47,7 @@ constexpr int kMaxK = 32;
 constexpr int kMaxE = 1024;
 constexpr int kMaxR = 32;
 constexpr int kDownRows = 64;  // output rows per down workgroup
-constexpr int kHChunkFloats = 8192;  // h floats staged in LDS per chunk of pairs (batched down)
+constexpr int kHChunkFloats = 4096;  // h floats staged in LDS per chunk of pairs (batched down)
 
 struct DecodeArgs {
     int L, B, K, E, S, d, f;
@@ -551,7 +551,7 @@ E0_DEV float down_dot(const u32x4 qv, float s, float b, const float (&h)[32], fl
 }
 
 template <int LPR>
-__global__ __launch_bounds__(kThreads) void decode_down_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, LPR <= 16 ? 3 : 1) void decode_down_kernel(DecodeArgs a) {
     constexpr int RPI = DownCfg<LPR>::RPI;
     constexpr int IT = DownCfg<LPR>::IT;
     __shared__ float s_acc[kMaxB][kDownRows];
@@ -679,7 +679,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(DecodeArgs a) {
         }
     };
     const int npairs = nu > 0 ? cload(uoff, nu) : 0;
-    const int chunk = kHChunkFloats / f;  // pairs per LDS chunk (f <= 2048: at least 4)
+    const int chunk = kHChunkFloats / f;  // pairs per LDS chunk (f <= 2048: at least 2)
     const int32_t *pslot = a.pslot + (int64_t)l * a.B * a.K;
     const float *wl = a.w + (int64_t)l * a.B * a.K;
     Wrows wc, wn;
