@@ -47,6 +47,7 @@ constexpr int kMaxK = 32;
 constexpr int kMaxE = 1024;
 constexpr int kMaxR = 32;
 constexpr int kDownRows = 64;  // output rows per down workgroup
+constexpr int kGuGroups = 8;         // row groups streamed per batched gate/up block
 constexpr int kHChunkFloats = 4096;  // h floats staged in LDS per chunk of pairs (batched down)
 
 struct DecodeArgs {
@@ -349,7 +350,7 @@ E0_DEV void x_pairs_m(const u32x4 v, uint32_t (&o)[4], float &sum) {
 // 2. gateup. Template: LPR lanes per row pass (d = 32 * LPR * NP), TC tokens
 // per register chunk, RB rows per lane group per iteration.
 // ---------------------------------------------------------------------------
-template <int LPR, int NP, int TC, int RB>
+template <int LPR, int NP, int TC, int RB, int G>
 __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
     constexpr int RPI = kWave / LPR;          // rows per wave instruction
     constexpr int ROWS_W = RPI * RB;          // rows per wave
@@ -390,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
         p_begin = u;
         p_count = 1;
     }
-    const int row_base = blockIdx.z * ROWS_B + wv * ROWS_W;
+    const int row_base = blockIdx.z * ROWS_B * G + wv * ROWS_W;
     if (row_base >= a.f) return;
 
     const int d = a.d;
@@ -446,80 +447,133 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
             }
         }
 
-        float acc[NV];
+        // G groups of ROWS_B rows per block (G > 1: the weight rows of group
+        // gi + 1 are requested before group gi is computed, so one block
+        // streams G groups with its loads in flight).
+        struct Wb {
+            u32x4 qv[RB][2][NP];
+            float sv[RB][2][NP], bv[RB][2][NP];
+        };
+        auto load_rows = [&](int rb_base, Wb &W) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
-        // Rows in batches of RBB: the batch's code loads are issued together,
-        // then consumed; the scheduling fence keeps the compiler from hoisting
-        // every batch's loads at once (register pressure).
-        constexpr int RBB = RB < 4 ? RB : 4;
-#pragma unroll
-        for (int rb0 = 0; rb0 < RB; rb0 += RBB) {
-            u32x4 qv[RBB][2][NP];
-            float sv[RBB][2][NP], bv[RBB][2][NP];
-#pragma unroll
-            for (int rr = 0; rr < RBB; ++rr) {
-                // Rows past the end are clamped to the last row (in-bounds
-                // loads, results never written) so the loads stay unconditional.
-                const int row = min(row_base + (rb0 + rr) * RPI + grp, a.f - 1);
+            for (int rr = 0; rr < RB; ++rr) {
+                const int row = min(rb_base + rr * RPI + grp, a.f - 1);  // clamped: in-bounds, never written
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
 #pragma unroll
                     for (int np = 0; np < NP; ++np) {
-                        const uint32_t col = (uint32_t)(np * LPR + gl);  // 32-element column block
-                        const uint32_t g = col / 2;                           // its group
-                        qv[rr][m][np] = ld128(qr[m], (uint32_t)row * (d / 2) + col * 16);
-                        sv[rr][m][np] = h2f(ld16(sr[m], sb_index((uint32_t)row, g, ngrp) * 2));
-                        bv[rr][m][np] = h2f(ld16(br[m], sb_index((uint32_t)row, g, ngrp) * 2));
+                        const uint32_t col = (uint32_t)(np * LPR + gl);
+                        const uint32_t g = col / 2;
+                        W.qv[rr][m][np] = ld128(qr[m], (uint32_t)row * (d / 2) + col * 16);
+                        W.sv[rr][m][np] = h2f(ld16(sr[m], sb_index((uint32_t)row, g, ngrp) * 2));
+                        W.bv[rr][m][np] = h2f(ld16(br[m], sb_index((uint32_t)row, g, ngrp) * 2));
                     }
                 }
             }
+        };
+        Wb Wc, Wn;
+        if constexpr (G > 1) load_rows(row_base, Wc);
+        for (int gi = 0; gi < G; ++gi) {
+            const int rbase = row_base + gi * ROWS_B;
+            if (rbase >= a.f) break;
+            float acc[NV];
 #pragma unroll
-            for (int rr = 0; rr < RBB; ++rr) {
-                const int rb = rb0 + rr;
+            for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
+            if constexpr (G > 1) {
+                if (gi + 1 < G) load_rows(rbase + ROWS_B, Wn);
 #pragma unroll
-                for (int m = 0; m < 2; ++m) {
+                for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-                    for (int np = 0; np < NP; ++np) {
-                        const float s = sv[rr][m][np];
-                        const float b16 = bv[rr][m][np] - 16.0f * s;
+                    for (int m = 0; m < 2; ++m) {
 #pragma unroll
-                        for (int t = 0; t < TC; ++t) {
-                            float dacc = 0.0f;
+                        for (int np = 0; np < NP; ++np) {
+                            const float s = Wc.sv[rb][m][np];
+                            const float b16 = Wc.bv[rb][m][np] - 16.0f * s;
 #pragma unroll
-                            for (int wd = 0; wd < 4; ++wd) dacc = dot_word(qv[rr][m][np][wd], xp[t][np][wd], dacc);
-                            acc[(m * RB + rb) * TC + t] += s * dacc + b16 * xs[t][np];
+                            for (int t = 0; t < TC; ++t) {
+                                float dacc = 0.0f;
+#pragma unroll
+                                for (int wd = 0; wd < 4; ++wd) dacc = dot_word(Wc.qv[rb][m][np][wd], xp[t][np][wd], dacc);
+                                acc[(m * RB + rb) * TC + t] += s * dacc + b16 * xs[t][np];
+                            }
                         }
                     }
                 }
+            } else {
+            // Rows in batches of RBB: the batch's code loads are issued together,
+            // then consumed; the scheduling fence keeps the compiler from hoisting
+            // every batch's loads at once (register pressure).
+            constexpr int RBB = RB < 4 ? RB : 4;
+    #pragma unroll
+            for (int rb0 = 0; rb0 < RB; rb0 += RBB) {
+                u32x4 qv[RBB][2][NP];
+                float sv[RBB][2][NP], bv[RBB][2][NP];
+    #pragma unroll
+                for (int rr = 0; rr < RBB; ++rr) {
+                    // Rows past the end are clamped to the last row (in-bounds
+                    // loads, results never written) so the loads stay unconditional.
+                    const int row = min(rbase + (rb0 + rr) * RPI + grp, a.f - 1);
+    #pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+    #pragma unroll
+                        for (int np = 0; np < NP; ++np) {
+                            const uint32_t col = (uint32_t)(np * LPR + gl);  // 32-element column block
+                            const uint32_t g = col / 2;                           // its group
+                            qv[rr][m][np] = ld128(qr[m], (uint32_t)row * (d / 2) + col * 16);
+                            sv[rr][m][np] = h2f(ld16(sr[m], sb_index((uint32_t)row, g, ngrp) * 2));
+                            bv[rr][m][np] = h2f(ld16(br[m], sb_index((uint32_t)row, g, ngrp) * 2));
+                        }
+                    }
+                }
+    #pragma unroll
+                for (int rr = 0; rr < RBB; ++rr) {
+                    const int rb = rb0 + rr;
+    #pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+    #pragma unroll
+                        for (int np = 0; np < NP; ++np) {
+                            const float s = sv[rr][m][np];
+                            const float b16 = bv[rr][m][np] - 16.0f * s;
+    #pragma unroll
+                            for (int t = 0; t < TC; ++t) {
+                                float dacc = 0.0f;
+    #pragma unroll
+                                for (int wd = 0; wd < 4; ++wd) dacc = dot_word(qv[rr][m][np][wd], xp[t][np][wd], dacc);
+                                acc[(m * RB + rb) * TC + t] += s * dacc + b16 * xs[t][np];
+                            }
+                        }
+                    }
+                }
+                __asm__ __volatile__("" ::: "memory");  // keep batches apart (register pressure)
             }
-            __asm__ __volatile__("" ::: "memory");  // keep batches apart (register pressure)
-        }
-
-        group_reduce_scatter<NV, LPR>(acc);
-
-        // Each lane now holds totals; gate values in the lower half of a row
-        // group, up values in the upper half (partner lane ^ LPR/2).
-        constexpr int PER = NV >= LPR ? NV / LPR : 1;
-        constexpr int DUP = NV >= LPR ? 1 : LPR / NV;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int vi = NV >= LPR ? gl * PER + j : gl / DUP;  // value index
-            const int m = vi / (RB * TC);
-            const int rb = (vi / TC) % RB;
-            const int t = vi % TC;
-            float val = acc[j];
-            const int row = row_base + rb * RPI + grp;
-            if (is_shared && a.r > 0 && row < a.f && tok[t] >= 0) {
-                const uint16_t *brow = a.lb[m] + (int64_t)l * (a.lb_ls[m] / 2) + (int64_t)row * a.r;
-                const float *av = a.lora_a + (((int64_t)l * a.B + tok[t]) * 3 + m) * a.r;
-                float dl = 0.0f;
-                for (int i = 0; i < a.r; ++i) dl += h2f(brow[i]) * av[i];
-                val += a.lscale * dl;
             }
-            const float other = __shfl_xor(val, LPR / 2);
-            if (m == 0 && (NV >= LPR || gl % DUP == 0) && row < a.f && tok[t] >= 0)
-                hrow(a, l, pid[t])[row] = silu(val) * other;
+
+            group_reduce_scatter<NV, LPR>(acc);
+
+            // Each lane now holds totals; gate values in the lower half of a row
+            // group, up values in the upper half (partner lane ^ LPR/2).
+            constexpr int PER = NV >= LPR ? NV / LPR : 1;
+            constexpr int DUP = NV >= LPR ? 1 : LPR / NV;
+    #pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                const int vi = NV >= LPR ? gl * PER + j : gl / DUP;  // value index
+                const int m = vi / (RB * TC);
+                const int rb = (vi / TC) % RB;
+                const int t = vi % TC;
+                float val = acc[j];
+                const int row = rbase + rb * RPI + grp;
+                if (is_shared && a.r > 0 && row < a.f && tok[t] >= 0) {
+                    const uint16_t *brow = a.lb[m] + (int64_t)l * (a.lb_ls[m] / 2) + (int64_t)row * a.r;
+                    const float *av = a.lora_a + (((int64_t)l * a.B + tok[t]) * 3 + m) * a.r;
+                    float dl = 0.0f;
+                    for (int i = 0; i < a.r; ++i) dl += h2f(brow[i]) * av[i];
+                    val += a.lscale * dl;
+                }
+                const float other = __shfl_xor(val, LPR / 2);
+                if (m == 0 && (NV >= LPR || gl % DUP == 0) && row < a.f && tok[t] >= 0)
+                    hrow(a, l, pid[t])[row] = silu(val) * other;
+            }
+            if constexpr (G > 1) Wc = Wn;
         }
     }
 }
@@ -1587,21 +1641,21 @@ Layout decode_layout(int L, int B, int K, int E, int f, int r, int n_dn = 0) {
     return o;
 }
 
-template <int LPR, int NP, int TC, int RB>
+template <int LPR, int NP, int TC, int RB, int G>
 void launch_gateup(const DecodeArgs &a, dim3 grid, hipStream_t st) {
-    hipLaunchKernelGGL((decode_gateup_kernel<LPR, NP, TC, RB>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_gateup_kernel<LPR, NP, TC, RB, G>), grid, dim3(kThreads), 0, st, a);
 }
 
-template <int TC, int RB>
+template <int TC, int RB, int G>
 bool dispatch_gateup(int lpr, int np, const DecodeArgs &a, dim3 grid, hipStream_t st) {
     switch (lpr * 8 + np) {
-        case 8 * 8 + 1: launch_gateup<8, 1, TC, RB>(a, grid, st); return true;
-        case 16 * 8 + 1: launch_gateup<16, 1, TC, RB>(a, grid, st); return true;
-        case 32 * 8 + 1: launch_gateup<32, 1, TC, RB>(a, grid, st); return true;
-        case 64 * 8 + 1: launch_gateup<64, 1, TC, RB>(a, grid, st); return true;
-        case 64 * 8 + 2: launch_gateup<64, 2, TC, RB>(a, grid, st); return true;
-        case 64 * 8 + 3: launch_gateup<64, 3, TC, RB>(a, grid, st); return true;
-        case 64 * 8 + 4: launch_gateup<64, 4, TC, RB>(a, grid, st); return true;
+        case 8 * 8 + 1: launch_gateup<8, 1, TC, RB, G>(a, grid, st); return true;
+        case 16 * 8 + 1: launch_gateup<16, 1, TC, RB, G>(a, grid, st); return true;
+        case 32 * 8 + 1: launch_gateup<32, 1, TC, RB, G>(a, grid, st); return true;
+        case 64 * 8 + 1: launch_gateup<64, 1, TC, RB, G>(a, grid, st); return true;
+        case 64 * 8 + 2: launch_gateup<64, 2, TC, RB, G>(a, grid, st); return true;
+        case 64 * 8 + 3: launch_gateup<64, 3, TC, RB, G>(a, grid, st); return true;
+        case 64 * 8 + 4: launch_gateup<64, 4, TC, RB, G>(a, grid, st); return true;
         default: return false;
     }
 }
@@ -1823,13 +1877,14 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
         constexpr int TC = 1, RB = 16;
         const int rpb = gateup_rows_per_block<TC, RB>(lpr_d);
         dim3 grid(L, ublocks, (f + rpb - 1) / rpb);
-        const bool ok = dispatch_gateup<TC, RB>(lpr_d, np, a, grid, st);
+        const bool ok = dispatch_gateup<TC, RB, 1>(lpr_d, np, a, grid, st);
         E0_REQUIRE(ok, E0_ERR_UNSUPPORTED_SHAPE);
     } else {
+        // Each block streams kGuGroups groups of rows of one expert.
         constexpr int TC = 4, RB = 4;
-        const int rpb = gateup_rows_per_block<TC, RB>(lpr_d);
+        const int rpb = gateup_rows_per_block<TC, RB>(lpr_d) * kGuGroups;
         dim3 grid(L, ublocks, (f + rpb - 1) / rpb);
-        const bool ok = dispatch_gateup<TC, RB>(lpr_d, np, a, grid, st);
+        const bool ok = dispatch_gateup<TC, RB, kGuGroups>(lpr_d, np, a, grid, st);
         E0_REQUIRE(ok, E0_ERR_UNSUPPORTED_SHAPE);
     }
     if ((s = e0_launch_status())) return s;
