@@ -38,6 +38,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -404,6 +406,140 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
         br[m] = make_rsrc(part_at(st->p[3 * m + 2], l, slot), (uint32_t)a.f * ngrp * 2);
     }
 
+    if constexpr (G > 1) {
+        // Blocks of G groups of ROWS_B rows: the expert's tokens go in chunks
+        // of 4, 2 or 1 (as many as remain, so few slots compute padding); for
+        // each chunk the block streams its G groups, the weight rows of group
+        // gi + 1 requested before group gi is computed.
+        struct Wb {
+            u32x4 qv[RB][2][NP];
+            float sv[RB][2][NP], bv[RB][2][NP];
+        };
+        auto load_rows = [&](int rb_base, Wb &W) {
+#pragma unroll
+            for (int rr = 0; rr < RB; ++rr) {
+                const int row = min(rb_base + rr * RPI + grp, a.f - 1);  // clamped: in-bounds, never written
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                    for (int np = 0; np < NP; ++np) {
+                        const uint32_t col = (uint32_t)(np * LPR + gl);
+                        const uint32_t g = col / 2;
+                        W.qv[rr][m][np] = ld128(qr[m], (uint32_t)row * (d / 2) + col * 16);
+                        W.sv[rr][m][np] = h2f(ld16(sr[m], sb_index((uint32_t)row, g, ngrp) * 2));
+                        W.bv[rr][m][np] = h2f(ld16(br[m], sb_index((uint32_t)row, g, ngrp) * 2));
+                    }
+                }
+            }
+        };
+        auto chunk = [&](auto tcc, int c0) {
+            constexpr int TCc = decltype(tcc)::value;
+            constexpr int NVc = 2 * RB * TCc;
+            int tok[TCc], pid[TCc];
+            uint32_t xp[TCc][NP][4][4];
+            float xs[TCc][NP];
+#pragma unroll
+            for (int t = 0; t < TCc; ++t) {
+                const int ci = c0 + t;
+                int p = -1, tk = -1;
+                if (ci < p_count) {
+                    if (is_shared) {
+                        tk = ci;
+                        p = a.B * a.K + ci;
+                    } else {
+                        p = plist[p_begin + ci];
+                        tk = p / a.K;
+                    }
+                }
+                tok[t] = tk;
+                pid[t] = p;
+                const int tl = tk >= 0 ? tk : 0;  // a padding slot reads token 0; never written
+#pragma unroll
+                for (int np = 0; np < NP; ++np) {
+                    float sm = 0.0f;
+#pragma unroll
+                    for (int wd = 0; wd < 4; ++wd) {
+                        const uint16_t *xr = a.x + ((int64_t)l * a.B + tl) * d + (np * LPR + gl) * 32 + wd * 8;
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(xr);
+                        x_pairs(v, xp[t][np][wd]);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            f16x2 hv = as_h2(v[j]);
+                            sm += (float)hv[0] + (float)hv[1];
+                        }
+                    }
+                    xs[t][np] = sm;
+                }
+            }
+            Wb Wc, Wn;
+            load_rows(row_base, Wc);
+            for (int gi = 0; gi < G; ++gi) {
+                const int rbase = row_base + gi * ROWS_B;
+                if (rbase >= a.f) break;
+                if (gi + 1 < G) load_rows(rbase + ROWS_B, Wn);
+                float acc[NVc];
+#pragma unroll
+                for (int i = 0; i < NVc; ++i) acc[i] = 0.0f;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                        for (int np = 0; np < NP; ++np) {
+                            const float sc = Wc.sv[rb][m][np];
+                            const float b16 = Wc.bv[rb][m][np] - 16.0f * sc;
+#pragma unroll
+                            for (int t = 0; t < TCc; ++t) {
+                                float dacc = 0.0f;
+#pragma unroll
+                                for (int wd = 0; wd < 4; ++wd) dacc = dot_word(Wc.qv[rb][m][np][wd], xp[t][np][wd], dacc);
+                                acc[(m * RB + rb) * TCc + t] += sc * dacc + b16 * xs[t][np];
+                            }
+                        }
+                    }
+                }
+                group_reduce_scatter<NVc, LPR>(acc);
+                // Gate values in the lower half of a row group, up values in
+                // the upper half (partner lane ^ LPR/2).
+                constexpr int PER = NVc >= LPR ? NVc / LPR : 1;
+                constexpr int DUP = NVc >= LPR ? 1 : LPR / NVc;
+#pragma unroll
+                for (int j = 0; j < PER; ++j) {
+                    const int vi = NVc >= LPR ? gl * PER + j : gl / DUP;  // value index
+                    const int m = vi / (RB * TCc);
+                    const int rb = (vi / TCc) % RB;
+                    const int t = vi % TCc;
+                    float val = acc[j];
+                    const int row = rbase + rb * RPI + grp;
+                    if (is_shared && a.r > 0 && row < a.f && tok[t] >= 0) {
+                        const uint16_t *brow = a.lb[m] + (int64_t)l * (a.lb_ls[m] / 2) + (int64_t)row * a.r;
+                        const float *av = a.lora_a + (((int64_t)l * a.B + tok[t]) * 3 + m) * a.r;
+                        float dl = 0.0f;
+                        for (int i = 0; i < a.r; ++i) dl += h2f(brow[i]) * av[i];
+                        val += a.lscale * dl;
+                    }
+                    const float other = __shfl_xor(val, LPR / 2);
+                    if (m == 0 && (NVc >= LPR || gl % DUP == 0) && row < a.f && tok[t] >= 0)
+                        hrow(a, l, pid[t])[row] = silu(val) * other;
+                }
+                Wc = Wn;
+            }
+        };
+        for (int c0 = 0; c0 < p_count;) {
+            const int rem = p_count - c0;
+            if (rem >= 3) {
+                chunk(std::integral_constant<int, 4>{}, c0);
+                c0 += 4;
+            } else if (rem == 2) {
+                chunk(std::integral_constant<int, 2>{}, c0);
+                c0 += 2;
+            } else {
+                chunk(std::integral_constant<int, 1>{}, c0);
+                c0 += 1;
+            }
+        }
+        return;
+    }
     for (int c0 = 0; c0 < p_count; c0 += TC) {
         // Token chunk: x slices as pairs, and their sums per pass.
         int tok[TC];
@@ -447,133 +583,80 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
             }
         }
 
-        // G groups of ROWS_B rows per block (G > 1: the weight rows of group
-        // gi + 1 are requested before group gi is computed, so one block
-        // streams G groups with its loads in flight).
-        struct Wb {
-            u32x4 qv[RB][2][NP];
-            float sv[RB][2][NP], bv[RB][2][NP];
-        };
-        auto load_rows = [&](int rb_base, Wb &W) {
+        float acc[NV];
 #pragma unroll
-            for (int rr = 0; rr < RB; ++rr) {
-                const int row = min(rb_base + rr * RPI + grp, a.f - 1);  // clamped: in-bounds, never written
+        for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
+        // Rows in batches of RBB: the batch's code loads are issued together,
+        // then consumed; the scheduling fence keeps the compiler from hoisting
+        // every batch's loads at once (register pressure).
+        constexpr int RBB = RB < 4 ? RB : 4;
+#pragma unroll
+        for (int rb0 = 0; rb0 < RB; rb0 += RBB) {
+            u32x4 qv[RBB][2][NP];
+            float sv[RBB][2][NP], bv[RBB][2][NP];
+#pragma unroll
+            for (int rr = 0; rr < RBB; ++rr) {
+                // Rows past the end are clamped to the last row (in-bounds
+                // loads, results never written) so the loads stay unconditional.
+                const int row = min(row_base + (rb0 + rr) * RPI + grp, a.f - 1);
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
 #pragma unroll
                     for (int np = 0; np < NP; ++np) {
-                        const uint32_t col = (uint32_t)(np * LPR + gl);
-                        const uint32_t g = col / 2;
-                        W.qv[rr][m][np] = ld128(qr[m], (uint32_t)row * (d / 2) + col * 16);
-                        W.sv[rr][m][np] = h2f(ld16(sr[m], sb_index((uint32_t)row, g, ngrp) * 2));
-                        W.bv[rr][m][np] = h2f(ld16(br[m], sb_index((uint32_t)row, g, ngrp) * 2));
+                        const uint32_t col = (uint32_t)(np * LPR + gl);  // 32-element column block
+                        const uint32_t g = col / 2;                           // its group
+                        qv[rr][m][np] = ld128(qr[m], (uint32_t)row * (d / 2) + col * 16);
+                        sv[rr][m][np] = h2f(ld16(sr[m], sb_index((uint32_t)row, g, ngrp) * 2));
+                        bv[rr][m][np] = h2f(ld16(br[m], sb_index((uint32_t)row, g, ngrp) * 2));
                     }
                 }
             }
-        };
-        Wb Wc, Wn;
-        if constexpr (G > 1) load_rows(row_base, Wc);
-        for (int gi = 0; gi < G; ++gi) {
-            const int rbase = row_base + gi * ROWS_B;
-            if (rbase >= a.f) break;
-            float acc[NV];
 #pragma unroll
-            for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
-            if constexpr (G > 1) {
-                if (gi + 1 < G) load_rows(rbase + ROWS_B, Wn);
+            for (int rr = 0; rr < RBB; ++rr) {
+                const int rb = rb0 + rr;
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
+                for (int m = 0; m < 2; ++m) {
 #pragma unroll
-                    for (int m = 0; m < 2; ++m) {
+                    for (int np = 0; np < NP; ++np) {
+                        const float s = sv[rr][m][np];
+                        const float b16 = bv[rr][m][np] - 16.0f * s;
 #pragma unroll
-                        for (int np = 0; np < NP; ++np) {
-                            const float s = Wc.sv[rb][m][np];
-                            const float b16 = Wc.bv[rb][m][np] - 16.0f * s;
+                        for (int t = 0; t < TC; ++t) {
+                            float dacc = 0.0f;
 #pragma unroll
-                            for (int t = 0; t < TC; ++t) {
-                                float dacc = 0.0f;
-#pragma unroll
-                                for (int wd = 0; wd < 4; ++wd) dacc = dot_word(Wc.qv[rb][m][np][wd], xp[t][np][wd], dacc);
-                                acc[(m * RB + rb) * TC + t] += s * dacc + b16 * xs[t][np];
-                            }
+                            for (int wd = 0; wd < 4; ++wd) dacc = dot_word(qv[rr][m][np][wd], xp[t][np][wd], dacc);
+                            acc[(m * RB + rb) * TC + t] += s * dacc + b16 * xs[t][np];
                         }
                     }
                 }
-            } else {
-            // Rows in batches of RBB: the batch's code loads are issued together,
-            // then consumed; the scheduling fence keeps the compiler from hoisting
-            // every batch's loads at once (register pressure).
-            constexpr int RBB = RB < 4 ? RB : 4;
-    #pragma unroll
-            for (int rb0 = 0; rb0 < RB; rb0 += RBB) {
-                u32x4 qv[RBB][2][NP];
-                float sv[RBB][2][NP], bv[RBB][2][NP];
-    #pragma unroll
-                for (int rr = 0; rr < RBB; ++rr) {
-                    // Rows past the end are clamped to the last row (in-bounds
-                    // loads, results never written) so the loads stay unconditional.
-                    const int row = min(rbase + (rb0 + rr) * RPI + grp, a.f - 1);
-    #pragma unroll
-                    for (int m = 0; m < 2; ++m) {
-    #pragma unroll
-                        for (int np = 0; np < NP; ++np) {
-                            const uint32_t col = (uint32_t)(np * LPR + gl);  // 32-element column block
-                            const uint32_t g = col / 2;                           // its group
-                            qv[rr][m][np] = ld128(qr[m], (uint32_t)row * (d / 2) + col * 16);
-                            sv[rr][m][np] = h2f(ld16(sr[m], sb_index((uint32_t)row, g, ngrp) * 2));
-                            bv[rr][m][np] = h2f(ld16(br[m], sb_index((uint32_t)row, g, ngrp) * 2));
-                        }
-                    }
-                }
-    #pragma unroll
-                for (int rr = 0; rr < RBB; ++rr) {
-                    const int rb = rb0 + rr;
-    #pragma unroll
-                    for (int m = 0; m < 2; ++m) {
-    #pragma unroll
-                        for (int np = 0; np < NP; ++np) {
-                            const float s = sv[rr][m][np];
-                            const float b16 = bv[rr][m][np] - 16.0f * s;
-    #pragma unroll
-                            for (int t = 0; t < TC; ++t) {
-                                float dacc = 0.0f;
-    #pragma unroll
-                                for (int wd = 0; wd < 4; ++wd) dacc = dot_word(qv[rr][m][np][wd], xp[t][np][wd], dacc);
-                                acc[(m * RB + rb) * TC + t] += s * dacc + b16 * xs[t][np];
-                            }
-                        }
-                    }
-                }
-                __asm__ __volatile__("" ::: "memory");  // keep batches apart (register pressure)
             }
-            }
+            __asm__ __volatile__("" ::: "memory");  // keep batches apart (register pressure)
+        }
 
-            group_reduce_scatter<NV, LPR>(acc);
+        group_reduce_scatter<NV, LPR>(acc);
 
-            // Each lane now holds totals; gate values in the lower half of a row
-            // group, up values in the upper half (partner lane ^ LPR/2).
-            constexpr int PER = NV >= LPR ? NV / LPR : 1;
-            constexpr int DUP = NV >= LPR ? 1 : LPR / NV;
-    #pragma unroll
-            for (int j = 0; j < PER; ++j) {
-                const int vi = NV >= LPR ? gl * PER + j : gl / DUP;  // value index
-                const int m = vi / (RB * TC);
-                const int rb = (vi / TC) % RB;
-                const int t = vi % TC;
-                float val = acc[j];
-                const int row = rbase + rb * RPI + grp;
-                if (is_shared && a.r > 0 && row < a.f && tok[t] >= 0) {
-                    const uint16_t *brow = a.lb[m] + (int64_t)l * (a.lb_ls[m] / 2) + (int64_t)row * a.r;
-                    const float *av = a.lora_a + (((int64_t)l * a.B + tok[t]) * 3 + m) * a.r;
-                    float dl = 0.0f;
-                    for (int i = 0; i < a.r; ++i) dl += h2f(brow[i]) * av[i];
-                    val += a.lscale * dl;
-                }
-                const float other = __shfl_xor(val, LPR / 2);
-                if (m == 0 && (NV >= LPR || gl % DUP == 0) && row < a.f && tok[t] >= 0)
-                    hrow(a, l, pid[t])[row] = silu(val) * other;
+        // Each lane now holds totals; gate values in the lower half of a row
+        // group, up values in the upper half (partner lane ^ LPR/2).
+        constexpr int PER = NV >= LPR ? NV / LPR : 1;
+        constexpr int DUP = NV >= LPR ? 1 : LPR / NV;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int vi = NV >= LPR ? gl * PER + j : gl / DUP;  // value index
+            const int m = vi / (RB * TC);
+            const int rb = (vi / TC) % RB;
+            const int t = vi % TC;
+            float val = acc[j];
+            const int row = row_base + rb * RPI + grp;
+            if (is_shared && a.r > 0 && row < a.f && tok[t] >= 0) {
+                const uint16_t *brow = a.lb[m] + (int64_t)l * (a.lb_ls[m] / 2) + (int64_t)row * a.r;
+                const float *av = a.lora_a + (((int64_t)l * a.B + tok[t]) * 3 + m) * a.r;
+                float dl = 0.0f;
+                for (int i = 0; i < a.r; ++i) dl += h2f(brow[i]) * av[i];
+                val += a.lscale * dl;
             }
-            if constexpr (G > 1) Wc = Wn;
+            const float other = __shfl_xor(val, LPR / 2);
+            if (m == 0 && (NV >= LPR || gl % DUP == 0) && row < a.f && tok[t] >= 0)
+                hrow(a, l, pid[t])[row] = silu(val) * other;
         }
     }
 }
