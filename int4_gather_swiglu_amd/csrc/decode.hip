@@ -460,13 +460,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
 #pragma unroll
                     for (int wd = 0; wd < 4; ++wd) {
                         const uint16_t *xr = a.x + ((int64_t)l * a.B + tl) * d + (np * LPR + gl) * 32 + wd * 8;
-                        const u32x4 v = *reinterpret_cast<const u32x4 *>(xr);
-                        x_pairs(v, xp[t][np][wd]);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            f16x2 hv = as_h2(v[j]);
-                            sm += (float)hv[0] + (float)hv[1];
-                        }
+                        x_pairs_m(*reinterpret_cast<const u32x4 *>(xr), xp[t][np][wd], sm);
                     }
                     xs[t][np] = sm;
                 }
@@ -486,14 +480,14 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
                     for (int m = 0; m < 2; ++m) {
 #pragma unroll
                         for (int np = 0; np < NP; ++np) {
-                            const float sc = Wc.sv[rb][m][np];
-                            const float b16 = Wc.bv[rb][m][np] - 16.0f * sc;
+                            const float sc = Wc.sv[rb][m][np] * kDenormScale;
+                            const float bi = Wc.bv[rb][m][np];
 #pragma unroll
                             for (int t = 0; t < TCc; ++t) {
                                 float dacc = 0.0f;
 #pragma unroll
-                                for (int wd = 0; wd < 4; ++wd) dacc = dot_word(Wc.qv[rb][m][np][wd], xp[t][np][wd], dacc);
-                                acc[(m * RB + rb) * TCc + t] += sc * dacc + b16 * xs[t][np];
+                                for (int wd = 0; wd < 4; ++wd) dacc = dot_word_m(Wc.qv[rb][m][np][wd], xp[t][np][wd], dacc);
+                                acc[(m * RB + rb) * TCc + t] += sc * dacc + bi * xs[t][np];
                             }
                         }
                     }
