@@ -154,15 +154,23 @@ def bench_decode(args, cfg, n_in, chain=False):
         raise RuntimeError(f"device error bits {int(pipe.err.item())}")
     # Distinct experts per layer per step (what the decode must read), from the
     # routing of the input steps, outside the timed region.
-    uniq = []
+    # The same replay gives the experts copied per step by consecutive slot
+    # updates (2 x bundle bytes each: read from the store, written to the pool).
+    uniq, copies = [], []
     for s in range(min(n_in, 16)):
-        route(0, s, False)
+        route(s % 2, s, False)
+        pipe.update(s % 2, (s - 1) % 2 if s else None, after_main=False)
+        pipe.join()
         torch.cuda.synchronize()
-        ids = pipe.idx[0].cpu().numpy().reshape(L, -1)
+        ids = pipe.idx[s % 2].cpu().numpy().reshape(L, -1)
         uniq.append(np.mean([len(np.unique(r)) for r in ids]))
+        if s:
+            copies.append(int(pipe.n_copied.sum().item()))
     dec_ms, upd_ms = mean_ms(ev_dec), mean_ms(ev_upd)
     algo_bytes = int(round(L * float(np.mean(uniq)) * bb))
     achieved = algo_bytes / (dec_ms * 1e-3) / 1e9
+    copy_bytes = int(round(2 * float(np.mean(copies)) * bb)) if copies else 0
+    step_s = wall / args.steps
     return dict(value=round(args.steps * B / wall, 2), unit=f"tok/s ({L}-layer MoE stack, batch {B})",
                 ms_per_step=round(wall * 1e3 / args.steps, 5),
                 config={"workload": f"{cfg.name}: {'chained' if chain else 'staged'} decode, {L} layers x {Ex} "
@@ -172,7 +180,13 @@ def bench_decode(args, cfg, n_in, chain=False):
                         "layers": L, "experts": Ex, "d_model": d, "d_ff": f, "top_k": K, "batch": B, "slots": S},
                 layer_tok_per_s=round(args.steps * B * L / wall, 1),
                 decode_call_us=round(dec_ms * 1e3, 2), route_and_slot_update_us=round(upd_ms * 1e3, 2),
-                slot_copies_last_step=int(pipe.n_copied.sum().item()), overlap=not args.no_overlap,
+                slot_copies_per_step=round(float(np.mean(copies)), 2) if copies else 0.0, overlap=not args.no_overlap,
+                step_hbm={"bytes_per_step": algo_bytes + copy_bytes, "decode_bytes": algo_bytes,
+                          "slot_copy_bytes": copy_bytes,
+                          "achieved": round((algo_bytes + copy_bytes) / step_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round((algo_bytes + copy_bytes) / step_s / 1e9 / HBM_PEAK_GBS, 4),
+                          "note": "all expert bytes one step moves (decode reads + slot-copy reads and writes) "
+                                  "over the measured step time"},
                 roofline={"bound": "hbm",
                           "kernel": ("e0_moe_chained_decode (one launch)" if chain else
                                      "e0_moe_staged_decode (one launch)" if B == 1 else
