@@ -386,19 +386,27 @@ def bench_prerouted(args, cfg, n_in):
     pipe.join()
 
     def step(t, rec):
+        # Step t: the side stream runs the heads of step t (routing of step t + 1,
+        # one call for all heads) and then the slot update for step t + 1, while
+        # the main stream decodes step t with the routing predicted one step
+        # earlier: the one-token lead lets the prediction and the staging of
+        # step t + 1 overlap step t's compute. The slot update waits for the
+        # decode of step t - 1 (it may evict that step's experts); the decode of
+        # step t + 1 waits for the update (join).
         c, n, p = t % 3, (t + 1) % 3, (t - 1) % 3
-        R[n, 0, 0].copy_(owner0[(t + 1) % n_in])
+        with torch.cuda.stream(pipe.side):
+            R[n, 0, 0].copy_(owner0[(t + 1) % n_in])
         if rec is not None:
-            ev_pre[rec][0].record()
-        pipe.predict(hin[t % n_in], R[c], R[p] if t > 0 else None, R[n], Wt[n])
+            ev_pre[rec][0].record(pipe.side)
+        pipe.predict(hin[t % n_in], R[c], R[p] if t > 0 else None, R[n], Wt[n], on_side=True)
         if rec is not None:
-            ev_pre[rec][1].record()
+            ev_pre[rec][1].record(pipe.side)
         pipe.update_ids(R[n, 1:], R[c, 1:])
         if rec is not None:
-            ev_dec[rec][0].record()
+            ev_dec[rec][0].record(pipe.main)
         pipe.decode_ids(R[c, 1:], Wt[c, 1:], hin[t % n_in, 1:], y)
         if rec is not None:
-            ev_dec[rec][1].record()
+            ev_dec[rec][1].record(pipe.main)
         pipe.join()
 
     wall = run_steps(args, step)

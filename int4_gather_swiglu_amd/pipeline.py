@@ -13,7 +13,9 @@ timeline; jaehun.me review, report 3.1):
 
 With the prerouter, the routing of step t+1 is the heads' prediction made at
 step t (one flush for all staged layers, then the slot update; koala.ai.kr
-prerouter section): PrerouterPipeline.
+prerouter section): PrerouterPipeline. With the one-token lead, the heads of
+step t and the slot update for step t+1 can run on the side stream while
+the main stream decodes step t (predict(..., on_side=True)).
 
 The update only writes slots whose experts are in neither set, and leaves the
 slot-table entries of step t's experts untouched, so it can run while step t
@@ -117,8 +119,10 @@ class PrerouterPipeline(StagedPipeline):
         hd = E.moe_dims(dims.d_model, heads.hidden, dims.n_experts, dims.top_k)
         self.ws_pre = torch.empty(E.workspace_bytes(E.E0_OP_PREROUTER, hd, L, B), dtype=torch.uint8, device=self.dev)
 
-    def predict(self, hin, r_cur, r_prev, r_next, w_next, logits_out=None):
+    def predict(self, hin, r_cur, r_prev, r_next, w_next, logits_out=None, on_side: bool = False):
         """Heads at step t: hin [L+1][B][d], r_cur / r_prev [L+1][B][K] (r_prev
-        may be None) -> r_next[1:], w_next[1:] (the routing of step t+1)."""
+        may be None) -> r_next[1:], w_next[1:] (the routing of step t+1), on the
+        main stream or (on_side) the side stream."""
         E.e0_prerouter(self.heads, self.L, self.B, self.dims.d_model, self.dims.n_experts, hin, r_cur, r_prev,
-                       self.route, r_next[1:], w_next[1:], logits_out, self.ws_pre, stream=self.main)
+                       self.route, r_next[1:], w_next[1:], logits_out, self.ws_pre,
+                       stream=self.side if on_side else self.main)
