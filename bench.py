@@ -439,30 +439,31 @@ def bench_prerouted(args, cfg, n_in):
 # HBM traffic of the dominant kernel, from committed counter passes
 # ---------------------------------------------------------------------------
 
-TRAFFIC_SOURCES = ("int4_gather_swiglu_amd/csrc/decode.hip", "int4_gather_swiglu_amd/csrc/e0_internal.h")
+TRAFFIC_SOURCES = {"decode35b": ("int4_gather_swiglu_amd/csrc/decode.hip", "int4_gather_swiglu_amd/csrc/e0_internal.h"),
+                   "prefill35b": ("int4_gather_swiglu_amd/csrc/prefill.hip", "int4_gather_swiglu_amd/csrc/e0_internal.h")}
 
 
-def kernel_sources_digest():
+def kernel_sources_digest(workload="decode35b"):
     import hashlib
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
+    for rel in TRAFFIC_SOURCES[workload]:
         with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
 def recorded_traffic(workload):
-    """HBM bytes per launch of the decode kernel from the committed FETCH_SIZE /
+    """HBM bytes per call of the dominant kernel(s) from the committed FETCH_SIZE /
     WRITE_SIZE passes (profiles/hbm_traffic_<workload>.txt), or None when there
     is no record or the kernel sources changed since it was taken."""
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"hbm_traffic_{workload}.txt")
-    if not os.path.exists(path):
+    if workload not in TRAFFIC_SOURCES or not os.path.exists(path):
         return None
     rec = [l for l in open(path).read().splitlines() if l.startswith("{")]
     if not rec:
         return None
     d = json.loads(rec[-1])
-    if d.get("sources_sha256") != kernel_sources_digest():
+    if d.get("sources_sha256") != kernel_sources_digest(workload):
         return None
     return int(d["hbm_bytes_per_launch"])
 
@@ -520,7 +521,7 @@ def main():
            "data": "synthetic (seeded; int4 codes U{0..15}, fp16 scale U(0.005,0.02), bias -8s(1+U(-0.1,0.1)))",
            "config": res.pop("config")}
     out.update(res)
-    if wl != "prefill35b" and "roofline" in out:
+    if "roofline" in out:
         out["roofline"]["traffic"] = recorded_traffic(wl)
     if not args.no_cpu_baseline and cpu is not None:
         out["cpu_baseline"] = cpu()
