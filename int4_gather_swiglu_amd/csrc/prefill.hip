@@ -54,7 +54,7 @@ struct PrefillArgs {
     int32_t *off;       // [E + 1] first sorted row of each expert
     int32_t *perm;      // [n] pair index at each sorted row
     float *wsort;       // [n] routing weight of the pair at each sorted row
-    int32_t *ntiles;    // [1]
+    int32_t *ntiles;    // [2]: all tiles, tiles of the heaviest class
     int32_t *tile_e;    // [max_tiles]
     int32_t *tile_m0;   // [max_tiles]
     uint16_t *H;        // [n][f] fp16
@@ -207,6 +207,7 @@ __global__ __launch_bounds__(kSortThreads) void prefill_sort_kernel(PrefillArgs 
     if (tid == 0) {
         a.off[E] = tot[0];
         a.ntiles[0] = tot[1] + tot[2] + tot[3];
+        a.ntiles[1] = tot[1];  // tiles of the heaviest class (the first ones of the list)
     }
 }
 
@@ -467,13 +468,25 @@ __global__ __launch_bounds__(kGemmThreads, 2) void prefill_gemm_kernel(PrefillAr
     __shared__ __attribute__((aligned(16))) uint16_t s_a[2][kTM * kARow];
     const int nN = (GATEUP ? a.f : a.d) / kCols;
     // The hardware deals block b to XCD b % 8 and dispatches in block order.
-    // Tile j of the list (heaviest class first) goes to XCD j % 8, and its
-    // column blocks take consecutive places on that XCD: the heavy tiles are
-    // spread over all XCDs (and their CUs) before any light one starts, and
-    // the column blocks of one tile re-read its rows from the same L2.
-    const int bi = blockIdx.x >> 3;
-    const int tile = (bi / nN) * 8 + (blockIdx.x & 7), nt = bi % nN;
-    if (tile >= a.ntiles[0]) return;
+    // Work items (tile, column block) of the heaviest class come first: XCD x
+    // takes the x-th of eight contiguous ranges of them (about one per CU),
+    // then the x-th contiguous range of the lighter ones. Contiguous ranges
+    // keep the tiles of one expert, and the column blocks of one tile, on one
+    // XCD, so its L2 fetches their weights and rows once; the heavy items are
+    // spread over all CUs before any light one starts.
+    const int nh = a.ntiles[1] * nN, nl = (a.ntiles[0] - a.ntiles[1]) * nN;
+    const int ph = (nh + 7) >> 3, pl = (nl + 7) >> 3;
+    const int bi = blockIdx.x >> 3, xcd = blockIdx.x & 7;
+    int wi;
+    if (bi < ph) {
+        wi = xcd * ph + bi;
+        if (wi >= nh) return;
+    } else {
+        const int li = xcd * pl + (bi - ph);
+        if (bi - ph >= pl || li >= nl) return;
+        wi = nh + li;
+    }
+    const int tile = wi / nN, nt = wi % nN;
     const int e = a.tile_e[tile], m0 = a.tile_m0[tile];
     const int m_end = a.off[e + 1];
     const int rows = m_end - m0;
@@ -520,7 +533,7 @@ PLayout prefill_layout(int T, int K, int E, int d, int f) {
     o.wsort = p;
     p = e0_align(p + sizeof(float) * (size_t)n);
     o.ntiles = p;
-    p = e0_align(p + sizeof(int32_t));
+    p = e0_align(p + sizeof(int32_t) * 2);
     o.tile_e = p;
     p = e0_align(p + sizeof(int32_t) * o.max_tiles);
     o.tile_m0 = p;
@@ -600,7 +613,9 @@ extern "C" e0_status e0_moe_sorted_prefill(const e0_moe_dims *dims, int32_t T, c
     if ((s = e0_launch_status())) return s;
     // Grids cover the largest tile count in whole groups of eight blocks;
     // blocks past the tiles the sort produced exit at once.
-    auto grid = [&](int cols) { return dim3((unsigned)(((int64_t)lay.max_tiles + 7) / 8 * (cols) * 8)); };
+    // Blocks for every work item with each of the two classes rounded up to a
+    // multiple of eight (blocks past the sort's items exit at once).
+    auto grid = [&](int cols) { return dim3((unsigned)((((int64_t)lay.max_tiles * (cols) + 7) / 8 + 1) * 8)); };
     hipLaunchKernelGGL((prefill_gemm_kernel<2, true>), grid(f / 128), dim3(kGemmThreads), 0, st, a);
     if ((s = e0_launch_status())) return s;
     if (d % 256 == 0)
