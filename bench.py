@@ -45,6 +45,9 @@ def parse():
                     choices=["decode35b", "prefill35b", "decode8b_b1", "decode8b_b32", "prerouted35b", "chain35b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overlap", action="store_true", help="run the slot update on the decode stream")
+    ap.add_argument("--host-store", action="store_true",
+                    help="keep the expert store in pinned host memory (the HBM slot pool as its cache; the slot "
+                         "update pulls changed experts over the host link)")
     ap.add_argument("--cpu-steps", type=int, default=0, help="oracle sample size (0 = auto)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference kernel for the "
@@ -86,6 +89,28 @@ def run_steps(args, step):
 # staged decode (35B and 8B tiers)
 # ---------------------------------------------------------------------------
 
+def expert_store(args, cfg, L, Ex, bb, dev, tag=None):
+    """The full expert store [L][E][bundle]: in HBM, or (--host-store) in pinned
+    host memory, filled layer by layer through a device staging buffer."""
+    import torch
+
+    from e0inputs import gen, gpu as G
+    kw = {} if tag is None else {"tag": tag}
+    if not args.host_store:
+        store = torch.empty((L, Ex, bb), dtype=torch.uint8, device=dev)
+        for l in range(L):
+            G.fill_experts(store[l].data_ptr(), bb, cfg.seed, l, range(Ex), cfg.d, cfg.f, **kw)
+        return store
+    store = torch.empty((L, Ex, bb), dtype=torch.uint8, pin_memory=True)
+    stage = torch.empty((Ex, bb), dtype=torch.uint8, device=dev)
+    for l in range(L):
+        G.fill_experts(stage.data_ptr(), bb, cfg.seed, l, range(Ex), cfg.d, cfg.f, **kw)
+        store[l].copy_(stage)
+    torch.cuda.synchronize()
+    del stage
+    return store
+
+
 def bench_decode(args, cfg, n_in, chain=False):
     import torch
 
@@ -98,9 +123,7 @@ def bench_decode(args, cfg, n_in, chain=False):
     bb = gen.bundle_bytes(d, f)
     # The full expert store filled on the GPU; per-step inputs drawn on the
     # host and resident in HBM before the timed region.
-    store = torch.empty((L, Ex, bb), dtype=torch.uint8, device=dev)
-    for l in range(L):
-        G.fill_experts(store[l].data_ptr(), bb, cfg.seed, l, range(Ex), d, f)
+    store = expert_store(args, cfg, L, Ex, bb, dev)
     pool = torch.zeros((L, S, bb), dtype=torch.uint8, device=dev)
     xs = torch.from_numpy(np.stack([np.stack([W.activations(cfg, t, l) for l in range(L)])
                                     for t in range(n_in)]).view(np.int16)).to(dev)
@@ -355,9 +378,7 @@ def bench_prerouted(args, cfg, n_in):
     def f16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
 
-    store = torch.empty((L, Ex, bb), dtype=torch.uint8, device=dev)
-    for l in range(L):
-        G.fill_experts(store[l].data_ptr(), bb, cfg.seed, l, range(Ex), d, f)
+    store = expert_store(args, cfg, L, Ex, bb, dev)
     pool = torch.zeros((L, S, bb), dtype=torch.uint8, device=dev)
     heads = [W.head(cfg, j) for j in range(L)]
     hd_t = [f16(np.stack([getattr(h, k) for h in heads])) for k in ("fc1_w", "fc1_b", "fc2_w", "fc2_b", "lin_w")]
@@ -521,6 +542,10 @@ def main():
            "data": "synthetic (seeded; int4 codes U{0..15}, fp16 scale U(0.005,0.02), bias -8s(1+U(-0.1,0.1)))",
            "config": res.pop("config")}
     out.update(res)
+    if wl != "prefill35b":
+        out["config"]["expert_store"] = "pinned host memory" if args.host_store else "HBM"
+        if args.host_store:
+            out["config"]["workload"] += ", expert store in pinned host memory (HBM slots as its cache)"
     if "roofline" in out:
         out["roofline"]["traffic"] = recorded_traffic(wl)
     if not args.no_cpu_baseline and cpu is not None:

@@ -27,6 +27,7 @@ constexpr int kMaxE = 4096;
 constexpr int kMaxS = 4096;
 constexpr int kCopyUnits = 4;  // 16-byte units per thread per copy block
 constexpr int kCopyChunk = kThreads * kCopyUnits * 16;
+constexpr int kHostCopyBlocks = 64;  // copy blocks when the store is in host memory
 
 struct SlotArgs {
     int L, BK, E, S;
@@ -144,12 +145,12 @@ struct CopyArgs {
     int contiguous;         // store and pool are bundle-contiguous
 };
 
-__global__ __launch_bounds__(kThreads) void slot_copy_kernel(CopyArgs a) {
-    const int l = blockIdx.x, i = blockIdx.y;
+// Chunk z of copy i of layer l (a no-op when layer l has fewer copies).
+E0_DEV void copy_chunk(const CopyArgs &a, int l, int i, int64_t z) {
     if (i >= cload(a.ncopy, l)) return;
     const int slot = cload(a.copy_slot, (int64_t)l * a.maxc + i);
     const int e = cload(a.copy_exp, (int64_t)l * a.maxc + i);
-    const int64_t u0 = (int64_t)blockIdx.z * (kCopyChunk / 16);
+    const int64_t u0 = z * (kCopyChunk / 16);
     u32x4 v[kCopyUnits];
     if (a.contiguous) {
         // Store and pool hold whole bundles: one linear range per expert.
@@ -188,6 +189,24 @@ __global__ __launch_bounds__(kThreads) void slot_copy_kernel(CopyArgs a) {
         if (dst_part[k] < 0) continue;
         u32x4 *dst = reinterpret_cast<u32x4 *>(const_cast<char *>(part_at(a.pool.p[dst_part[k]], l, slot))) + dst_off[k];
         __builtin_nontemporal_store(v[k], dst);
+    }
+}
+
+// Store in device memory: one block per (layer, copy, chunk).
+__global__ __launch_bounds__(kThreads) void slot_copy_kernel(CopyArgs a) {
+    copy_chunk(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Store in host memory: a few blocks walk every (layer, copy, chunk). Reads
+// over the host link take microseconds each; one block per chunk would hold
+// every CU while it waits and starve the decode that runs beside the
+// update, while a few blocks with 16 KB each in flight already keep the link
+// busy.
+__global__ __launch_bounds__(kThreads) void slot_copy_strided_kernel(CopyArgs a, int L, int64_t chunks) {
+    const int64_t items = (int64_t)L * a.maxc * chunks;
+    for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
+        const int64_t z = w % chunks, li = w / chunks;
+        copy_chunk(a, (int)(li / a.maxc), (int)(li % a.maxc), z);
     }
 }
 
@@ -237,8 +256,9 @@ SlotLayout slot_layout(int L, int BK, int S, int E) {
 // the device (then the copy pulls the changed experts over the host link).
 // Each part's address is resolved to the one the device uses; a part in
 // memory the device cannot reach rejects the call before anything is enqueued.
-bool resolve_for_device(const e0_stack &in, e0_stack &out) {
+bool resolve_for_device(const e0_stack &in, e0_stack &out, bool &host) {
     out = in;
+    host = false;
     for (int i = 0; i < 9; ++i) {
         hipPointerAttribute_t at{};
         if (hipPointerGetAttributes(&at, in.part[i].ptr) != hipSuccess) {
@@ -248,6 +268,7 @@ bool resolve_for_device(const e0_stack &in, e0_stack &out) {
         if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) continue;
         if (at.type != hipMemoryTypeHost || !at.devicePointer) return false;
         out.part[i].ptr = at.devicePointer;
+        host = true;
     }
     return true;
 }
@@ -275,7 +296,8 @@ extern "C" e0_status e0_slot_update(const e0_moe_dims *dims, int32_t L, int32_t 
     E0_REQUIRE(ws && ws_bytes >= lay.total && (reinterpret_cast<uintptr_t>(ws) & 255) == 0, E0_ERR_CAPACITY);
     if (L == 0) return E0_OK;
     e0_stack dstore;
-    E0_REQUIRE(resolve_for_device(*store, dstore), E0_ERR_INVALID_ARG);
+    bool host_store = false;
+    E0_REQUIRE(resolve_for_device(*store, dstore, host_store), E0_ERR_INVALID_ARG);
 
     CopyArgs c{};
     const int64_t qb = (int64_t)d * f / 2, sb = (int64_t)d * f / kGroup * 2;
@@ -304,6 +326,9 @@ extern "C" e0_status e0_slot_update(const e0_moe_dims *dims, int32_t L, int32_t 
     c.store = to_stack(dstore);
     c.pool = to_stack(*pool);
     c.contiguous = stack_contiguous(&dstore, c.part_end) && stack_contiguous(pool, c.part_end);
-    hipLaunchKernelGGL(slot_copy_kernel, dim3(L, lay.maxc, (unsigned)chunks), dim3(kThreads), 0, st, c);
+    if (host_store)
+        hipLaunchKernelGGL(slot_copy_strided_kernel, dim3(kHostCopyBlocks), dim3(kThreads), 0, st, c, (int)L, chunks);
+    else
+        hipLaunchKernelGGL(slot_copy_kernel, dim3(L, lay.maxc, (unsigned)chunks), dim3(kThreads), 0, st, c);
     return e0_launch_status();
 }
