@@ -1167,6 +1167,8 @@ constexpr int kFuseThreads = 256;
 constexpr int kFuseWaves = kFuseThreads / kWave;
 constexpr int kBlk = 36;  // dwords per h block: 16 hi pairs, 16 lo pairs, the sum of each half (+ pad)
 constexpr int kBlkSum = 32;
+constexpr int kChainSplit = 2;  // wavefronts per h half block in chained gate/up items
+constexpr int kChainD = 2048;   // d_model of chained calls (one 32-input slice per lane)
 
 E0_DEV uint64_t *gu_flags(const DecodeArgs &a, int l) { return a.flags + a.L + (int64_t)l * a.units * a.nch; }
 
@@ -1199,7 +1201,7 @@ E0_DEV void fused_lora_item(const DecodeArgs &a, int l) {
 // of layer l, x = fp16(r / sqrt(mean(r^2) + eps) * g), r the residual after
 // layer l - 1 (the call's input for layer 0). Waits (whole workgroup) for the
 // down items of layer l - 1, which publish the residual.
-E0_DEV void chain_input(const DecodeArgs &a, int l, u32x4 (&xr)[4]) {
+E0_DEV void chain_input(const DecodeArgs &a, int l, u32x4 (&xr)[4], float *s_r) {
     const int lane = threadIdx.x & 63;
     const int d = a.d;
     u32x4 gv[4];
@@ -1217,14 +1219,22 @@ E0_DEV void chain_input(const DecodeArgs &a, int l, u32x4 (&xr)[4]) {
     } else {
         if (!wait_ready(a.dflags + (int64_t)(l - 1) * a.n_dn, a.n_dn, a.epoch) && threadIdx.x == 0)
             set_err(a.err, E0_DEV_SYNC_TIMEOUT);
-        const uint64_t *src = reinterpret_cast<const uint64_t *>(a.r_out + (int64_t)(l - 1) * d + lane * 32);
-        uint64_t t[16];
+        // The residual is read once per workgroup (device-coherent loads, 32
+        // bytes per thread) and shared through LDS: every wavefront of every
+        // item reading all of it made a queue at the same lines.
+        constexpr int kPer = kChainD / 2 / kFuseThreads;
+        const uint64_t *src = reinterpret_cast<const uint64_t *>(a.r_out + (int64_t)(l - 1) * d);
+        uint64_t t[kPer];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) t[i] = coherent_load(src + i);
+        for (int i = 0; i < kPer; ++i) t[i] = coherent_load(src + threadIdx.x + i * kFuseThreads);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            rv[2 * i] = __builtin_bit_cast(float, (uint32_t)t[i]);
-            rv[2 * i + 1] = __builtin_bit_cast(float, (uint32_t)(t[i] >> 32));
+        for (int i = 0; i < kPer; ++i) reinterpret_cast<uint64_t *>(s_r)[threadIdx.x + i * kFuseThreads] = t[i];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(s_r + lane * 32 + 4 * i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rv[4 * i + j] = v[j];
         }
     }
     float ss = 0.0f;
@@ -1258,16 +1268,26 @@ E0_DEV int routed_slot(const DecodeArgs &a, int l, int k, int &bits) {
 // w % 2 of h block c = 2cg + w / 2, i.e. the gate and up rows of 16 hidden
 // units, streamed in 4 batches of 4 units with the loads of the next batch in
 // flight while one is computed. It publishes its half block with its own
-// flag, so the wavefronts of an item never wait on each other.
+// flag, so the wavefronts of an item never wait on each other. Chained items
+// cover 32 hidden units: wavefronts 2j and 2j + 1 take 8 units each of half
+// block 2cg + j (both batches requested before the wait), meet in LDS, and
+// the first publishes the half block.
 template <int NP, bool SHARED, bool CHAIN = false>
-E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *s_small) {
-    constexpr int NBT = 16 / kFlatBatch;  // batches per half block
+E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *s_small, float *s_r = nullptr) {
+    // Chained items: kChainSplit wavefronts share a half block (the wait for
+    // the previous layer puts every batch on the critical path, so each
+    // wavefront computes fewer of them).
+    constexpr int kWph = CHAIN ? kChainSplit : 1;         // wavefronts per half block
+    constexpr int kUnitsW = kHalfBlk / kWph;              // hidden units per wavefront
+    constexpr int NBT = kUnitsW / kFlatBatch;             // batches per wavefront
     const int lane = threadIdx.x & 63, wv = wave_id();
-    const int c = cg * 2 + wv / 2, hf = wv % 2;
+    const int hb = cg * (kFuseWaves / kWph) + wv / kWph;  // half block of the unit
+    const int sub = wv % kWph;
+    const int c = hb / 2, hf = hb % 2;
     const int d = a.d, ngrp = d / kGroup;
-    const int row0 = c * 32 + hf * 16;
-    float *s_av = s_small;                        // [2r] LoRA A x
-    float *s_hv = s_small + 2 * kMaxR + wv * 16;  // this wavefront's 16 h values
+    const int row0 = c * 32 + hf * 16 + sub * kUnitsW;
+    float *s_av = s_small;                                 // [2r] LoRA A x
+    float *s_hv = s_small + 2 * kMaxR + (wv / kWph) * 16;  // the half block's 16 h values
     // Prologue: the kernel arguments in one batch, the slot, the weight loads
     // of the first two batches, then the loads of x (in-order load counters:
     // x issued earlier would put its latency in front of the weight loads).
@@ -1326,17 +1346,15 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *
                 }
             }
         };
-        Stage A, B, C, D;  // C, D: chained items only
+        Stage A, B;
         load(0, A);
         load(1, B);
         u32x4 xr[NP][4];
         if constexpr (CHAIN) {
             // Chained: every batch's weights are requested before the wait for
             // the previous layer, so none of them is on the critical path.
-            static_assert(NP == 1 && !SHARED && NBT == 4, "chained items: d_model 2048, routed experts");
-            load(2, C);
-            load(3, D);
-            chain_input(a, l, xr[0]);
+            static_assert(NP == 1 && !SHARED && NBT == 2, "chained items: d_model 2048, routed experts");
+            chain_input(a, l, xr[0], s_r);
         } else {
 #pragma unroll
             for (int np = 0; np < NP; ++np)
@@ -1385,13 +1403,11 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *
                 val += a.lscale * dl;
             }
             const float other = __shfl_xor(val, 32);
-            if (m == 0 && lane % DUP == 0) s_hv[bt * kFlatBatch + rr] = silu(val) * other;
+            if (m == 0 && lane % DUP == 0) s_hv[sub * kUnitsW + bt * kFlatBatch + rr] = silu(val) * other;
         };
         if constexpr (CHAIN) {
             compute(0, A);
             compute(1, B);
-            compute(2, C);
-            compute(3, D);
         } else {
             // Two-stage pipeline; the empty asm statements keep the compiler from
             // hoisting later batches' loads (register pressure) or sinking them.
@@ -1409,10 +1425,16 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *
                 }
             }
         }
-    } else if (lane < 16) {
-        s_hv[lane] = 0.0f;
+    } else if (lane < kUnitsW) {
+        s_hv[sub * kUnitsW + lane] = 0.0f;
     }
-    wave_lds_sync();
+    if constexpr (CHAIN) {
+        // The wavefronts of a half block meet in LDS; the first one publishes.
+        __syncthreads();
+        if (sub) return;
+    } else {
+        wave_lds_sync();
+    }
     // This wavefront's half of the h block: hi/lo fp16 pairs of h with the
     // odd pairs scaled by 1/16 (the form dot_word_m2 takes), and the half's sum.
     {
@@ -1615,6 +1637,7 @@ __global__ __launch_bounds__(kFuseThreads) void decode_fused_kernel(DecodeArgs a
     __shared__ __attribute__((aligned(16))) uint32_t s_hb[(KM + 1) * LPR * kBlk];
     __shared__ float s_hsh[32 * LPR];
     __shared__ float s_small[2 * kMaxR + kFuseWaves * 16];
+    __shared__ __attribute__((aligned(16))) float s_rr[CHAIN ? kChainD : 4];  // chained: the layer's input residual
     // Item order: the lora items, then steps s = 0 .. L + lag - 1, step s
     // holding the gate/up items of layer s (s < L) followed by the down items
     // of layer s - lag (s >= lag). Every down item comes after all gate/up
@@ -1645,10 +1668,10 @@ __global__ __launch_bounds__(kFuseThreads) void decode_fused_kernel(DecodeArgs a
         r = item % n2;
     }
     if (gu) {
-        const int per_u = a.nch / kFuseWaves;  // items per unit
+        const int per_u = a.nch / (CHAIN ? kFuseWaves / kChainSplit : kFuseWaves);  // items per unit
         const int u = r / per_u, cg = r % per_u;
         if constexpr (CHAIN)
-            fused_gateup_item<NP, false, true>(a, l, u, cg, s_small);
+            fused_gateup_item<NP, false, true>(a, l, u, cg, s_small, s_rr);
         else if (u < a.K)
             fused_gateup_item<NP, false>(a, l, u, cg, s_small);
         else
@@ -1686,6 +1709,11 @@ struct Layout {
 // Output rows per wavefront of a down item of the single-launch kernel: at
 // least two load instructions per unit, so its scales are one 4/8/16-byte load.
 int fused_rows_per_wave(int K, int lpr_f) { return (K <= 4 || lpr_f == 8) ? 16 : 8; }
+
+// Chained calls: each down item waits for its layer, so its compute is on the
+// critical path; with d_ff 512 a wavefront takes 8 output rows (twice the
+// items per layer, half the work after the wait).
+int chain_rows_per_wave(int K, int lpr_f) { return lpr_f == 16 ? 8 : fused_rows_per_wave(K, lpr_f); }
 
 // n_dn: down items per layer of a chained call (their ready flags), else 0.
 Layout decode_layout(int L, int B, int K, int E, int f, int r, int n_dn = 0) {
@@ -1761,7 +1789,7 @@ void launch_fused(const DecodeArgs &a, int lpr_f, bool small, dim3 grid, hipStre
                 else hipLaunchKernelGGL((decode_fused_kernel<1, 8, 8, 16, true>), grid, dim3(kFuseThreads), 0, st, a);
                 break;
             case 16:
-                if (small) hipLaunchKernelGGL((decode_fused_kernel<1, 16, 4, 16, true>), grid, dim3(kFuseThreads), 0, st, a);
+                if (small) hipLaunchKernelGGL((decode_fused_kernel<1, 16, 4, 8, true>), grid, dim3(kFuseThreads), 0, st, a);
                 else hipLaunchKernelGGL((decode_fused_kernel<1, 16, 8, 8, true>), grid, dim3(kFuseThreads), 0, st, a);
                 break;
             default:
@@ -1971,7 +1999,7 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
 
 size_t e0_chain_workspace_bytes(const e0_moe_dims *dims, int32_t L) {
     if (!dims || L < 0 || !fused_shape_ok(dims->d_model, dims->d_ff, dims->top_k)) return 0;
-    const int n_dn = dims->d_model / (kFuseWaves * fused_rows_per_wave(dims->top_k, f_lpr(dims->d_ff)));
+    const int n_dn = dims->d_model / (kFuseWaves * chain_rows_per_wave(dims->top_k, f_lpr(dims->d_ff)));
     return decode_layout(L, 1, dims->top_k, dims->n_experts, dims->d_ff, 0, n_dn).total;
 }
 
@@ -1990,8 +2018,8 @@ extern "C" e0_status e0_moe_chained_decode(const e0_moe_dims *dims, int32_t L, c
                  reinterpret_cast<uintptr_t>(r_out)) & 15) == 0, E0_ERR_INVALID_ARG);
     E0_REQUIRE(stack_ok(pool, 0, 8), E0_ERR_INVALID_ARG);
     const int lpr_f = f_lpr(f);
-    const int rw = fused_rows_per_wave(K, lpr_f);
-    const int64_t n_gu = (int64_t)K * (f / kHalfBlk / kFuseWaves), n_dn = d / (kFuseWaves * rw);
+    const int rw = chain_rows_per_wave(K, lpr_f);
+    const int64_t n_gu = (int64_t)K * (f / kHalfBlk / (kFuseWaves / kChainSplit)), n_dn = d / (kFuseWaves * rw);
     const Layout lay = decode_layout(L, 1, K, E, f, 0, (int)n_dn);
     E0_REQUIRE(ws && ws_bytes >= lay.total && (reinterpret_cast<uintptr_t>(ws) & 255) == 0, E0_ERR_CAPACITY);
     E0_REQUIRE((int64_t)L * (n_gu + n_dn) <= (int64_t)INT32_MAX, E0_ERR_CAPACITY);
