@@ -507,11 +507,27 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
     if (i >= tot) return;
     const int t = (int)(i / (a.d / 4));
     const int c4 = (int)(i % (a.d / 4));
+    // Rows are loaded before their ids are checked (every row of Yb is in
+    // bounds; a skipped pair's row holds stale bytes and is dropped), so the
+    // id loads and the row loads are in flight together.
     f32x4 s = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k = 0; k < a.K; ++k) {
+    int k = 0;
+    for (; k + 4 <= a.K; k += 4) {
+        int e[4];
+        f32x4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            e[i] = a.idx[(int64_t)t * a.K + k + i];
+            v[i] = *reinterpret_cast<const f32x4 *>(a.Yb + ((int64_t)t * a.K + k + i) * a.d + 4 * c4);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (e[i] >= 0 && e[i] < a.E) s += v[i];
+    }
+    for (; k < a.K; ++k) {
         const int e = a.idx[(int64_t)t * a.K + k];
-        if (e < 0 || e >= a.E) continue;
-        s += *reinterpret_cast<const f32x4 *>(a.Yb + ((int64_t)t * a.K + k) * a.d + 4 * c4);
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(a.Yb + ((int64_t)t * a.K + k) * a.d + 4 * c4);
+        if (e >= 0 && e < a.E) s += v;
     }
     *reinterpret_cast<f32x4 *>(a.y + (int64_t)t * a.d + 4 * c4) = s;
 }
