@@ -308,6 +308,34 @@ e0_status e0_moe_chained_decode(const e0_moe_dims *dims, int32_t L, const float 
                                 const e0_stack *pool, float *y, float *r_out, void *ws, size_t ws_bytes,
                                 int32_t *dev_err, void *stream);
 
+/*
+ * e0_lora_merge_requant — a LoRA delta merged into an int4 group-64 matrix and
+ * requantised: the alternative the pages weigh against serving the recovery
+ * LoRA unmerged (jaehun.me review, the paragraph on not merging, citing the
+ * report's section 3.3 and its retention measure 1 - |U - M| / |U - B|;
+ * xyznot.com FAQ on why the recovery LoRA stays unmerged: deltas of RMS about
+ * 1e-3 sit below one 4-bit step, so requantisation erases most of them).
+ * Per row i and column c, in fp32 with every operation rounded to nearest
+ * (no fused multiply-add):
+ *   w = s[i][g] * q[i][c] + b[i][g]                       (g = c / 64)
+ *   t = sum over k = 0 .. r-1, in order, of B[i][k] * A[k][c]
+ *   w' = w + alpha_over_r * t
+ * then per (row, group), with lo/hi the group's least/largest w':
+ *   s' = fp16((hi - lo) / 15),  b' = fp16(lo),
+ *   q' = s' == 0 ? 0 : min(15, max(0, round_half_even((w' - b') / s'))).
+ *  rows, cols: rows % 8 == 0, cols % 64 == 0, rows * cols < 2^31; r in 1 .. 64.
+ *  q, q_out: device uint32 [rows][cols/8] (code c at bits 4*(c%8) of word
+ *  c/8); s, b, s_out, b_out: device fp16 bit patterns in the stacks' 8-row
+ *  tiles ([rows/8][cols/64][8], as in e0_stack); lora_b: device fp16
+ *  [rows][r]; lora_a: device fp16 [r][cols]. All pointers 16-byte aligned;
+ *  outputs must not overlap the inputs. One launch on `stream`; nothing is
+ *  allocated. Errors: E0_ERR_INVALID_ARG / E0_ERR_UNSUPPORTED_SHAPE before
+ *  any launch, E0_ERR_HIP on a launch failure.
+ */
+e0_status e0_lora_merge_requant(int32_t rows, int32_t cols, const uint32_t *q, const uint16_t *s, const uint16_t *b,
+                                const uint16_t *lora_b, const uint16_t *lora_a, int32_t r, float alpha_over_r,
+                                uint32_t *q_out, uint16_t *s_out, uint16_t *b_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

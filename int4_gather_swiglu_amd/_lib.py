@@ -19,7 +19,8 @@ E0_DEV_BAD_ID, E0_DEV_NOT_RESIDENT, E0_DEV_NO_SLOT = 1, 2, 4
  E0_OP_CHAINED_DECODE) = range(6)
 
 EXPORTS = ["e0_abi_version", "e0_status_string", "e0_workspace_bytes", "e0_route", "e0_prerouter",
-           "e0_moe_staged_decode", "e0_moe_sorted_prefill", "e0_slot_update", "e0_moe_chained_decode"]
+           "e0_moe_staged_decode", "e0_moe_sorted_prefill", "e0_slot_update", "e0_moe_chained_decode",
+           "e0_lora_merge_requant"]
 
 
 class E0Error(RuntimeError):
@@ -90,8 +91,9 @@ def lib() -> C.CDLL:
                                      C.POINTER(Stack), vp, vp, sz, vp, vp]
         L.e0_moe_chained_decode.argtypes = [C.POINTER(MoeDims), i32, vp, vp, C.c_float, vp, vp, vp, i32,
                                             C.POINTER(Stack), vp, vp, vp, sz, vp, vp]
+        L.e0_lora_merge_requant.argtypes = [i32, i32, vp, vp, vp, vp, vp, i32, C.c_float, vp, vp, vp, vp]
         for n in ("e0_route", "e0_prerouter", "e0_moe_staged_decode", "e0_moe_sorted_prefill", "e0_slot_update",
-                  "e0_moe_chained_decode"):
+                  "e0_moe_chained_decode", "e0_lora_merge_requant"):
             getattr(L, n).restype = C.c_int32
         _LIB = L
     return _LIB
@@ -193,6 +195,13 @@ def e0_moe_chained_decode(dims: MoeDims, L: int, r_in, norm_w, eps: float, idx, 
                                        _ptr(w), _ptr(slot_of), S, C.byref(pool), _ptr(y), _ptr(r_out), _ptr(ws),
                                        ws.numel() * ws.element_size() if ws is not None else 0, _ptr(dev_err),
                                        _stream(stream)), "e0_moe_chained_decode")
+
+
+def e0_lora_merge_requant(rows: int, cols: int, q, s, b, lora_b, lora_a, r: int, alpha_over_r: float, q_out, s_out,
+                          b_out, stream=None):
+    _check(lib().e0_lora_merge_requant(rows, cols, _ptr(q), _ptr(s), _ptr(b), _ptr(lora_b), _ptr(lora_a), r,
+                                       C.c_float(alpha_over_r), _ptr(q_out), _ptr(s_out), _ptr(b_out),
+                                       _stream(stream)), "e0_lora_merge_requant")
 
 
 def e0_moe_sorted_prefill(dims: MoeDims, T: int, x, idx, w, layer: Stack, y, ws, dev_err, stream=None):

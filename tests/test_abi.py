@@ -136,6 +136,25 @@ def test_prefill_validation():
     assert rc == E.E0_ERR_UNSUPPORTED_SHAPE
 
 
+def test_lora_merge_validation():
+    L = E.lib()
+    F = C.c_void_p(FAKE)
+    G = C.c_void_p(FAKE + 0x100000)  # distinct, non-overlapping fake ranges for the outputs
+    H = C.c_void_p(FAKE + 0x200000)
+    I = C.c_void_p(FAKE + 0x300000)
+    call = L.e0_lora_merge_requant
+    # rows not a multiple of 8, cols not a multiple of 64, rank out of range
+    assert call(12, 128, F, F, F, F, F, 16, C.c_float(2.0), G, H, I, None) == E.E0_ERR_UNSUPPORTED_SHAPE
+    assert call(16, 100, F, F, F, F, F, 16, C.c_float(2.0), G, H, I, None) == E.E0_ERR_UNSUPPORTED_SHAPE
+    assert call(16, 128, F, F, F, F, F, 0, C.c_float(2.0), G, H, I, None) == E.E0_ERR_UNSUPPORTED_SHAPE
+    assert call(16, 128, F, F, F, F, F, 65, C.c_float(2.0), G, H, I, None) == E.E0_ERR_UNSUPPORTED_SHAPE
+    # null, misaligned, non-finite scale, output overlapping an input
+    assert call(16, 128, None, F, F, F, F, 16, C.c_float(2.0), G, H, I, None) == E.E0_ERR_INVALID_ARG
+    assert call(16, 128, C.c_void_p(FAKE + 2), F, F, F, F, 16, C.c_float(2.0), G, H, I, None) == E.E0_ERR_INVALID_ARG
+    assert call(16, 128, F, F, F, F, F, 16, C.c_float(float("nan")), G, H, I, None) == E.E0_ERR_INVALID_ARG
+    assert call(16, 128, F, F, F, F, F, 16, C.c_float(2.0), F, H, I, None) == E.E0_ERR_INVALID_ARG
+
+
 def test_binding_has_no_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(E, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(E, "_LIB", None)
