@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode35b",
-                    choices=["decode35b", "prefill35b", "decode8b_b1", "decode8b_b32", "prerouted35b", "chain35b"])
+                    choices=["decode35b", "prefill35b", "decode8b_b1", "decode8b_b32", "prerouted35b", "chain35b",
+                             "merge35b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overlap", action="store_true", help="run the slot update on the decode stream")
     ap.add_argument("--host-store", action="store_true",
@@ -361,6 +362,102 @@ def cpu_prefill(cfg, n_tok):
 
 
 # ---------------------------------------------------------------------------
+# merged LoRA (N4): the recovery LoRA merged into the shared experts and requantised
+# ---------------------------------------------------------------------------
+
+def bench_merge(args, cfg):
+    """One step = e0_lora_merge_requant on the gate, up and down matrices of the
+    shared expert of every layer (the prerouted tier's 32 layers, its recovery
+    LoRA r = 16, alpha / r = 2). Retention 1 - |U - M| / |U - B| of the merged
+    matrices is reported from the last step (fp32 torch on the device)."""
+    import torch
+
+    from e0inputs import gen, workloads as W
+    from int4_gather_swiglu_amd import _lib as E
+
+    dev = torch.device("cuda:0")
+    L, d, f, r, a = cfg.L, cfg.d, cfg.shared_f, cfg.lora_r, cfg.lora_alpha_over_r
+    t = lambda x, dt: torch.from_numpy(np.ascontiguousarray(x).view(dt)).to(dev)
+    mats = []  # per (layer, matrix): inputs, outputs, shapes
+    for l in range(L):
+        sh = W.shared_expert(cfg, l)
+        lo = W.lora(cfg, l)
+        for m in range(3):
+            q, sc, bi = sh[m]
+            rows, cols = q.shape[0], q.shape[1] * 8
+            la, lb = lo[m]
+            ins = (t(q, np.int32), t(gen._tile8(sc).reshape(-1), np.int16), t(gen._tile8(bi).reshape(-1), np.int16),
+                   t(lb.view(np.uint16), np.int16), t(la.view(np.uint16), np.int16))
+            outs = (torch.empty_like(ins[0]), torch.empty_like(ins[1]), torch.empty_like(ins[2]))
+            mats.append((rows, cols, ins, outs))
+    def step(_t, _rec):
+        for rows, cols, ins, outs in mats:
+            E.e0_lora_merge_requant(rows, cols, *ins, r, a, *outs)
+
+    wall = run_steps(args, step)
+    # The timed steps are bound by the host's launch rate (96 small launches
+    # per step). The kernel's own duration comes from a pass after them: a
+    # short spin kernel ahead of each step lets the host enqueue its 96
+    # launches before the GPU reaches them, so the event pair around them
+    # measures the kernels back to back.
+    ev = events(5)
+    for i in range(5):
+        torch.cuda._sleep(4_000_000)
+        ev[i][0].record()
+        step(0, None)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = mean_ms(ev) / len(mats)  # per call
+    nbytes = sum(2 * (rows * cols // 2 + 2 * rows * cols // 64 * 2) + 2 * r * (rows + cols) for rows, cols, _, _ in mats)
+    gbs = nbytes / len(mats) / (ms * 1e-3) / 1e9
+
+    def deq(q, sc, bi, rows, cols):
+        sh = torch.arange(8, device=dev, dtype=torch.int64) * 4
+        c = ((q.to(torch.int64).reshape(rows, cols // 8, 1) & 0xFFFFFFFF) >> sh) & 15
+        untile = lambda v: v.view(torch.float16).reshape(rows // 8, cols // 64, 8).permute(0, 2, 1).reshape(rows, cols // 64)
+        return (untile(sc).float().repeat_interleave(64, 1) * c.reshape(rows, cols).float()
+                + untile(bi).float().repeat_interleave(64, 1))
+
+    num = den = 0.0
+    for rows, cols, ins, outs in mats:
+        base = deq(ins[0], ins[1], ins[2], rows, cols)
+        delta = a * (ins[3].view(torch.float16).float().reshape(rows, r) @ ins[4].view(torch.float16).float().reshape(r, cols))
+        merged = deq(outs[0], outs[1], outs[2], rows, cols)
+        num += float(((base + delta - merged) ** 2).sum())
+        den += float((delta ** 2).sum())
+    retention = 1.0 - (num / den) ** 0.5
+    rms = (den / sum(rows * cols for rows, cols, _, _ in mats)) ** 0.5
+    return dict(value=round(args.steps * len(mats) / wall, 1),
+                unit=f"merged int4 g64 matrices/s ({L} layers x 3 shared-expert matrices per step)",
+                ms_per_step=round(wall * 1e3 / args.steps, 5), gpu_ms_per_step=round(ms * len(mats), 5),
+                config={"workload": f"{cfg.name} shared experts: LoRA r={r}, alpha/r={a} merged into int4 g64 "
+                                    f"and requantised, {L} layers x (gate, up {f}x{d}; down {d}x{f})",
+                        "layers": L, "d_model": d, "d_ff_shared": f, "lora_r": r},
+                merge_call_us=round(ms * 1e3, 2),  # kernels back to back (pass after the timed steps)
+                retention={"value": round(retention, 4), "delta_rms": float(f"{rms:.3g}"),
+                           "measure": "1 - |U - M| / |U - B| over all merged matrices (Frobenius)"},
+                roofline={"bound": "hbm", "kernel": "e0_lora_merge_requant", "achieved": round(gbs, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                          "traffic": None, "algorithmic_bytes_per_launch": nbytes // len(mats),
+                          "unit_of_work": "int4 matrix read + written (codes, scales, biases) + LoRA A and B"})
+
+
+def cpu_merge(cfg):
+    from e0inputs import workloads as W
+    from oracle import merge as M
+
+    sh, lo = W.shared_expert(cfg, 0), W.lora(cfg, 0)
+    t0 = time.perf_counter()
+    for m in range(3):
+        q, sc, bi = sh[m]
+        la, lb = lo[m]
+        M.merge_requant(q, sc, bi, lb.view(np.uint16), la.view(np.uint16), cfg.lora_alpha_over_r)
+    dt = time.perf_counter() - t0
+    return {"value": round(3 / dt, 3), "unit": "merged int4 g64 matrices/s", "cores": 1, "kind": "oracle",
+            "sample": f"the 3 shared-expert matrices of layer 0 through the oracle's fp32 numpy merge; {dt:.2f} s"}
+
+
+# ---------------------------------------------------------------------------
 # prerouted pipeline (35B tier, 32 staged layers)
 # ---------------------------------------------------------------------------
 
@@ -532,17 +629,21 @@ def main():
     elif wl == "chain35b":
         res = bench_decode(args, W.CHAIN35, 16, chain=True)
         cpu = (lambda: cpu_chain(W.CHAIN35, args.cpu_steps))
+    elif wl == "merge35b":
+        res = bench_merge(args, W.PREROUTED35)
+        cpu = (lambda: cpu_merge(W.PREROUTED35))
     else:
         res = bench_prerouted(args, W.PREROUTED35, 32)
     out = {"metric": METRIC, "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None,
            "dtype": ("int4 g64 weights dequantised to fp16, fp16 MFMA, fp32 accumulate" if wl == "prefill35b"
+                     else "int4 g64 weights and fp16 LoRA, fp32 merge, int4 g64 out" if wl == "merge35b"
                      else "int4 g64 weights, fp16 activations, fp32 accumulate"),
            "data": "synthetic (seeded; int4 codes U{0..15}, fp16 scale U(0.005,0.02), bias -8s(1+U(-0.1,0.1)))",
            "config": res.pop("config")}
     out.update(res)
-    if wl != "prefill35b":
+    if wl not in ("prefill35b", "merge35b"):
         out["config"]["expert_store"] = "pinned host memory" if args.host_store else "HBM"
         if args.host_store:
             out["config"]["workload"] += ", expert store in pinned host memory (HBM slots as its cache)"

@@ -7,8 +7,10 @@
 // group's least value, codes rounded half to even); every fp32 operation is
 // rounded to nearest on its own, so the codes do not depend on contraction.
 //
-// One thread per (row, 64-column group); a workgroup covers one 8-row tile
-// and 32 groups, so its scale and bias stores are 512 contiguous bytes each.
+// Eight lanes per (row, 64-column group), one code word each; the group's
+// least and largest value meet by lane shuffles. A workgroup covers one 8-row
+// tile and 4 groups; its slice of A and its rows of B are staged in LDS
+// first. A 512 x 2048 matrix is 2048 wavefronts.
 #include "e0_internal.h"
 
 #include <cmath>
@@ -16,7 +18,7 @@
 namespace {
 
 constexpr int kMergeThreads = 256;
-constexpr int kGroupsPerBlock = kMergeThreads / 8;
+constexpr int kGroupsPerBlock = kMergeThreads / 64;  // 8 rows x 4 groups x 8 lanes
 constexpr int kMaxRank = 64;
 
 // Single fp32 operations rounded to nearest; fp-contract is off here, so no
@@ -31,6 +33,8 @@ E0_DEV float mul_rn(float x, float y) {
 }
 E0_DEV float div_rn(float x, float y) { return x / y; }  // IEEE division (correctly rounded by default)
 
+// Eight consecutive lanes share one (row, group); lane j of them owns columns
+// 8j .. 8j + 7 of the group (its code word j).
 __global__ __launch_bounds__(kMergeThreads) void lora_merge_kernel(int rows, int cols, const uint32_t *q,
                                                                   const uint16_t *s, const uint16_t *b,
                                                                   const uint16_t *lb, const uint16_t *la, int r,
@@ -38,70 +42,80 @@ __global__ __launch_bounds__(kMergeThreads) void lora_merge_kernel(int rows, int
                                                                   uint16_t *b_out) {
     const int ngrp = cols / kGroup;
     const int tile = blockIdx.y;
-    const int row = tile * 8 + (threadIdx.x & 7);
-    const int g = blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 3);
-    if (g >= ngrp || row >= rows) return;
-    const int64_t sb = ((int64_t)tile * ngrp + g) * 8 + (threadIdx.x & 7);  // 8-row tile layout
+    const int sub = threadIdx.x & 7, pair = threadIdx.x >> 3;
+    const int rl = pair & 7, gl = pair >> 3;
+    const int row = tile * 8 + rl;
+    const int g0 = blockIdx.x * kGroupsPerBlock, g = g0 + gl;
+    // The workgroup's slice of A (r rows x its groups) and the 8 rows of B go
+    // to LDS once, all loads in flight together.
+    extern __shared__ __attribute__((aligned(16))) uint16_t s_ab[];
+    constexpr int kUnits = kGroupsPerBlock * kGroup / 8;  // 16-byte units per row of the slice
+    uint16_t *s_a = s_ab;                                 // [r][kGroupsPerBlock * 64]
+    uint16_t *s_b = s_ab + r * kUnits * 8;                // [8][r]
+    for (int i = threadIdx.x; i < r * kUnits; i += kMergeThreads) {
+        const int k = i / kUnits, u = i % kUnits;
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (g0 + u / 8 < ngrp) v = *reinterpret_cast<const u32x4 *>(la + (int64_t)k * cols + g0 * kGroup + u * 8);
+        *reinterpret_cast<u32x4 *>(s_a + (k * kUnits + u) * 8) = v;
+    }
+    for (int i = threadIdx.x; i < 8 * r; i += kMergeThreads) s_b[i] = lb[(int64_t)(tile * 8 + i / r) * r + i % r];
+    __syncthreads();
+    const bool on = g < ngrp;  // lanes past the last group compute on zeros and store nothing
+    const int64_t sb = ((int64_t)tile * ngrp + (on ? g : 0)) * 8 + rl;  // 8-row tile layout
     const float sc = (float)__builtin_bit_cast(f16, s[sb]);
     const float bi = (float)__builtin_bit_cast(f16, b[sb]);
-    const u32x4 *qw = reinterpret_cast<const u32x4 *>(q + (int64_t)row * (cols / 8) + g * 8);
-    const u32x4 qa = qw[0], qb = qw[1];
-    const uint32_t words[8] = {qa[0], qa[1], qa[2], qa[3], qb[0], qb[1], qb[2], qb[3]};
-    // t for the 64 columns, k outermost (each column's sum in k order).
-    float w[kGroup];
+    const uint32_t word = q[(int64_t)row * (cols / 8) + (on ? g : 0) * 8 + sub];
+
+    // t for this lane's 8 columns, k outermost (each column's sum in k order).
+    float w[8];
 #pragma unroll
-    for (int c = 0; c < kGroup; ++c) w[c] = 0.0f;
+    for (int c = 0; c < 8; ++c) w[c] = 0.0f;
     for (int k = 0; k < r; ++k) {
-        const float bk = (float)__builtin_bit_cast(f16, lb[(int64_t)row * r + k]);
-        const u32x4 *arow = reinterpret_cast<const u32x4 *>(la + (int64_t)k * cols + g * kGroup);
+        const float bk = (float)__builtin_bit_cast(f16, s_b[rl * r + k]);
+        const u32x4 av = *reinterpret_cast<const u32x4 *>(s_a + (k * kUnits + gl * 8 + sub) * 8);
 #pragma unroll
-        for (int ch = 0; ch < 8; ++ch) {  // 8 columns: one 16-byte load of A
-            const u32x4 av = arow[ch];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t aw = av[j];
-                const f16x2 a2 = as_h2(aw);
-                w[ch * 8 + 2 * j] = add_rn(w[ch * 8 + 2 * j], mul_rn(bk, (float)a2[0]));
-                w[ch * 8 + 2 * j + 1] = add_rn(w[ch * 8 + 2 * j + 1], mul_rn(bk, (float)a2[1]));
-            }
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t aw = av[j];
+            const f16x2 a2 = as_h2(aw);
+            w[2 * j] = add_rn(w[2 * j], mul_rn(bk, (float)a2[0]));
+            w[2 * j + 1] = add_rn(w[2 * j + 1], mul_rn(bk, (float)a2[1]));
         }
     }
-    // w' = (s q + b) + alpha t.
+    // w' = (s q + b) + alpha t; the group's least and largest over its 8 lanes.
+    float lo, hi;
 #pragma unroll
-    for (int c = 0; c < kGroup; ++c) {
-        const float code = (float)((words[c / 8] >> (4 * (c % 8))) & 15u);
+    for (int c = 0; c < 8; ++c) {
+        const float code = (float)((word >> (4 * c)) & 15u);
         const float dq = add_rn(mul_rn(sc, code), bi);
         w[c] = add_rn(dq, mul_rn(alpha, w[c]));
+        lo = c ? (w[c] < lo ? w[c] : lo) : w[c];
+        hi = c ? (w[c] > hi ? w[c] : hi) : w[c];
     }
-    float lo = w[0], hi = w[0];
 #pragma unroll
-    for (int c = 1; c < kGroup; ++c) {
-        lo = w[c] < lo ? w[c] : lo;
-        hi = w[c] > hi ? w[c] : hi;
+    for (int o = 1; o < 8; o <<= 1) {
+        const float lo2 = __shfl_xor(lo, o), hi2 = __shfl_xor(hi, o);
+        lo = lo2 < lo ? lo2 : lo;
+        hi = hi2 > hi ? hi2 : hi;
     }
     const f16 s16 = (f16)div_rn(add_rn(hi, -lo), 15.0f);
     const f16 b16 = (f16)lo;
     const float s2 = (float)s16, b2 = (float)b16;
-    uint32_t out[8];
+    uint32_t out = 0;
 #pragma unroll
-    for (int ch = 0; ch < 8; ++ch) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float v = 0.0f;
-            if (s2 != 0.0f) {
-                v = __builtin_rintf(div_rn(add_rn(w[ch * 8 + j], -b2), s2));
-                v = v < 0.0f ? 0.0f : v > 15.0f ? 15.0f : v;
-            }
-            word |= (uint32_t)v << (4 * j);
+    for (int c = 0; c < 8; ++c) {
+        float v = 0.0f;
+        if (s2 != 0.0f) {
+            v = __builtin_rintf(div_rn(add_rn(w[c], -b2), s2));
+            v = v < 0.0f ? 0.0f : v > 15.0f ? 15.0f : v;
         }
-        out[ch] = word;
+        out |= (uint32_t)v << (4 * c);
     }
-    u32x4 *qo = reinterpret_cast<u32x4 *>(q_out + (int64_t)row * (cols / 8) + g * 8);
-    qo[0] = u32x4{out[0], out[1], out[2], out[3]};
-    qo[1] = u32x4{out[4], out[5], out[6], out[7]};
-    s_out[sb] = __builtin_bit_cast(uint16_t, s16);
-    b_out[sb] = __builtin_bit_cast(uint16_t, b16);
+    if (!on) return;
+    q_out[(int64_t)row * (cols / 8) + g * 8 + sub] = out;
+    if (sub == 0) {
+        s_out[sb] = __builtin_bit_cast(uint16_t, s16);
+        b_out[sb] = __builtin_bit_cast(uint16_t, b16);
+    }
 }
 
 bool overlaps(const void *p, size_t np, const void *q, size_t nq) {
@@ -133,7 +147,8 @@ extern "C" e0_status e0_lora_merge_requant(int32_t rows, int32_t cols, const uin
         for (int p = o + 1; p < 3; ++p) E0_REQUIRE(!overlaps(outs[o], nout[o], outs[p], nout[p]), E0_ERR_INVALID_ARG);
     }
     const dim3 grid((unsigned)((cols / kGroup + kGroupsPerBlock - 1) / kGroupsPerBlock), (unsigned)(rows / 8));
-    hipLaunchKernelGGL(lora_merge_kernel, grid, dim3(kMergeThreads), 0, static_cast<hipStream_t>(stream), rows, cols,
+    const size_t lds = ((size_t)r * kGroupsPerBlock * kGroup + 8 * (size_t)r) * 2;  // A slice + B rows
+    hipLaunchKernelGGL(lora_merge_kernel, grid, dim3(kMergeThreads), lds, static_cast<hipStream_t>(stream), rows, cols,
                        q, s, b, lora_b, lora_a, r, alpha_over_r, q_out, s_out, b_out);
     return e0_launch_status();
 }
