@@ -277,6 +277,31 @@ e0_status e0_slot_update(const e0_moe_dims *dims, int32_t L, int32_t B, int32_t 
                          void *stream);
 
 /*
+ * e0_slot_update_lru — e0_slot_update with the pool kept as a per-layer
+ * least-recently-used hot set of the store: an HBM budget of S slots per
+ * layer, larger than one step needs and smaller than the store, that keeps
+ * the experts used most recently (koala.ai.kr on the hot path of resident
+ * experts; jaehun.me review, report 3.2 on whole-layer residency). Same
+ * arguments and limits as e0_slot_update, plus:
+ *  last_use: device int32 [L][S], the last step at which each slot's expert
+ *  was wanted (-1 = never; initialise to -1 with the tables); step: this
+ *  update's step number, >= 0, increasing from call to call.
+ * Rule per layer: every expert of U' already resident stays and its slot's
+ * last_use becomes `step` (a hit); the i-th missing expert of U' in
+ * ascending id takes the i-th candidate slot (empty, or holding an expert in
+ * neither U' nor U) in ascending (last_use, slot) order, and that slot's
+ * last_use becomes `step` (a miss: the expert least recently used is
+ * evicted). Every wanted expert is resident afterwards, so the decode stays
+ * exact; only the copy count depends on the policy. n_copied counts the
+ * misses. Errors as e0_slot_update; E0_ERR_INVALID_ARG also for a null
+ * last_use or a negative step.
+ */
+e0_status e0_slot_update_lru(const e0_moe_dims *dims, int32_t L, int32_t B, int32_t S, const int32_t *next_idx,
+                             const int32_t *cur_idx, int32_t *slot_of, int32_t *expert_of, int32_t *last_use,
+                             int32_t step, const e0_stack *store, const e0_stack *pool, int32_t *n_copied, void *ws,
+                             size_t ws_bytes, int32_t *dev_err, void *stream);
+
+/*
  * e0_moe_chained_decode — one token through L stacked layers in one call, the
  * input of each layer computed from the output of the one before (the pages
  * stage the next layers' experts ahead so that their weight reads overlap the

@@ -20,7 +20,7 @@ E0_DEV_BAD_ID, E0_DEV_NOT_RESIDENT, E0_DEV_NO_SLOT = 1, 2, 4
 
 EXPORTS = ["e0_abi_version", "e0_status_string", "e0_workspace_bytes", "e0_route", "e0_prerouter",
            "e0_moe_staged_decode", "e0_moe_sorted_prefill", "e0_slot_update", "e0_moe_chained_decode",
-           "e0_lora_merge_requant"]
+           "e0_lora_merge_requant", "e0_slot_update_lru"]
 
 
 class E0Error(RuntimeError):
@@ -89,11 +89,13 @@ def lib() -> C.CDLL:
                                             vp, vp]
         L.e0_slot_update.argtypes = [C.POINTER(MoeDims), i32, i32, i32, vp, vp, vp, vp, C.POINTER(Stack),
                                      C.POINTER(Stack), vp, vp, sz, vp, vp]
+        L.e0_slot_update_lru.argtypes = [C.POINTER(MoeDims), i32, i32, i32, vp, vp, vp, vp, vp, i32, C.POINTER(Stack),
+                                     C.POINTER(Stack), vp, vp, sz, vp, vp]
         L.e0_moe_chained_decode.argtypes = [C.POINTER(MoeDims), i32, vp, vp, C.c_float, vp, vp, vp, i32,
                                             C.POINTER(Stack), vp, vp, vp, sz, vp, vp]
         L.e0_lora_merge_requant.argtypes = [i32, i32, vp, vp, vp, vp, vp, i32, C.c_float, vp, vp, vp, vp]
         for n in ("e0_route", "e0_prerouter", "e0_moe_staged_decode", "e0_moe_sorted_prefill", "e0_slot_update",
-                  "e0_moe_chained_decode", "e0_lora_merge_requant"):
+                  "e0_moe_chained_decode", "e0_lora_merge_requant", "e0_slot_update_lru"):
             getattr(L, n).restype = C.c_int32
         _LIB = L
     return _LIB
@@ -216,6 +218,14 @@ def e0_slot_update(dims: MoeDims, L: int, B: int, S: int, next_idx, cur_idx, slo
                                 _ptr(expert_of), C.byref(store), C.byref(pool), _ptr(n_copied), _ptr(ws),
                                 ws.numel() * ws.element_size() if ws is not None else 0, _ptr(dev_err),
                                 _stream(stream)), "e0_slot_update")
+
+
+def e0_slot_update_lru(dims: MoeDims, L: int, B: int, S: int, next_idx, cur_idx, slot_of, expert_of, last_use,
+                       step: int, store: Stack, pool: Stack, n_copied, ws, dev_err, stream=None):
+    _check(lib().e0_slot_update_lru(C.byref(dims), L, B, S, _ptr(next_idx), _ptr(cur_idx), _ptr(slot_of),
+                                    _ptr(expert_of), _ptr(last_use), step, C.byref(store), C.byref(pool),
+                                    _ptr(n_copied), _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+                                    _ptr(dev_err), _stream(stream)), "e0_slot_update_lru")
 
 
 def heads_from_tensors(fc1_w, fc1_b, fc2_w, fc2_b, lin_w) -> PrerouterHeads:

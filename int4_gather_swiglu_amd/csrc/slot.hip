@@ -14,6 +14,15 @@
 // the lowest such slot, because each assignment only removes its own slot
 // from the candidates.
 //
+// Hot-set variant (e0_slot_update_lru): a pool larger than one step needs,
+// kept as a per-layer least-recently-used cache of the store (koala.ai.kr on
+// the hot path of resident experts; jaehun.me review, report 3.2 on whole-
+// layer residency): every wanted expert, resident or placed, gets the step
+// as its slot's last use, and the candidates are taken in ascending (last
+// use, slot) order instead of ascending slot, so a miss evicts the expert
+// least recently used. The result stays exact: every wanted expert is made
+// resident before the decode reads it.
+//
 // Two launches: plan (one workgroup per layer: sets, compaction, tables, copy
 // list) and copy (many workgroups: 16-byte vector copies of the nine parts,
 // one linear range per expert when store and pool hold whole bundles, with
@@ -41,6 +50,8 @@ struct SlotArgs {
     int32_t *copy_slot;       // ws [L][maxc]
     int32_t *copy_exp;        // ws [L][maxc]
     int maxc;
+    int32_t *last_use;        // [L][S] last step each slot was wanted (-1 never), or null: lowest-slot rule
+    int32_t step;
 };
 
 // Exclusive scan of one int per thread over the block.
@@ -69,6 +80,7 @@ __global__ __launch_bounds__(kThreads) void slot_plan_kernel(SlotArgs a) {
     __shared__ unsigned char s_keep[kMaxE];
     __shared__ int s_miss[kMaxS];
     __shared__ int s_free[kMaxS];
+    __shared__ int s_order[kMaxS];
     __shared__ int s_scan[kThreads / 64];
     const int l = blockIdx.x, tid = threadIdx.x;
     int32_t *slot_of = a.slot_of + (int64_t)l * a.E;
@@ -98,9 +110,12 @@ __global__ __launch_bounds__(kThreads) void slot_plan_kernel(SlotArgs a) {
     }
     int mtot;
     int mb = block_scan(nm, s_scan, mtot);
+    int32_t *last_use = a.last_use ? a.last_use + (int64_t)l * a.S : nullptr;
     for (int e = tid * eper; e < (tid + 1) * eper && e < a.E; ++e) {
         const int s = slot_of[e];
-        if (s_want[e] && !(s >= 0 && s < a.S && expert_of[s] == e)) s_miss[mb++] = e;
+        const bool resident = s >= 0 && s < a.S && expert_of[s] == e;
+        if (s_want[e] && !resident) s_miss[mb++] = e;
+        if (s_want[e] && resident && last_use) last_use[s] = a.step;  // a hit (never a candidate below)
     }
     // Free slots (ascending): empty, or holding an expert in neither set.
     const int sper = (a.S + kThreads - 1) / kThreads;
@@ -116,15 +131,32 @@ __global__ __launch_bounds__(kThreads) void slot_plan_kernel(SlotArgs a) {
         if ((o < 0 || o >= a.E) || (!s_want[o] && !s_keep[o])) s_free[fb++] = s;
     }
     __syncthreads();
+    // Hot set: candidates in ascending (last use, slot) order; each one's
+    // rank is the number of candidates before it.
+    const int *cand = s_free;
+    if (last_use) {
+        for (int i = tid; i < ftot; i += kThreads) {
+            const int si = s_free[i], ki = last_use[si];
+            int rank = 0;
+            for (int j = 0; j < ftot; ++j) {
+                const int sj = s_free[j], kj = last_use[sj];
+                rank += kj < ki || (kj == ki && sj < si);
+            }
+            s_order[rank] = si;
+        }
+        __syncthreads();
+        cand = s_order;
+    }
 
     const int n = mtot < ftot ? mtot : ftot;
     if (tid == 0 && mtot > ftot) set_err(a.err, E0_DEV_NO_SLOT);
     for (int i = tid; i < n; i += kThreads) {
-        const int s = s_free[i], e = s_miss[i];
+        const int s = cand[i], e = s_miss[i];
         const int old = expert_of[s];
         if (old >= 0 && old < a.E && slot_of[old] == s) slot_of[old] = -1;
         expert_of[s] = e;
         slot_of[e] = s;
+        if (last_use) last_use[s] = a.step;
         a.copy_slot[(int64_t)l * a.maxc + i] = s;
         a.copy_exp[(int64_t)l * a.maxc + i] = e;
     }
@@ -280,11 +312,12 @@ size_t e0_slot_workspace_bytes(const e0_moe_dims *dims, int32_t L, int32_t B, in
     return slot_layout(L, B * dims->top_k, S, dims->n_experts).total;
 }
 
-extern "C" e0_status e0_slot_update(const e0_moe_dims *dims, int32_t L, int32_t B, int32_t S,
-                                    const int32_t *next_idx, const int32_t *cur_idx, int32_t *slot_of,
-                                    int32_t *expert_of, const e0_stack *store, const e0_stack *pool,
-                                    int32_t *n_copied, void *ws, size_t ws_bytes, int32_t *dev_err, void *stream) {
-    e0_clear_stale_error();
+namespace {
+
+e0_status slot_update_impl(const e0_moe_dims *dims, int32_t L, int32_t B, int32_t S, const int32_t *next_idx,
+                           const int32_t *cur_idx, int32_t *slot_of, int32_t *expert_of, int32_t *last_use,
+                           int32_t step, const e0_stack *store, const e0_stack *pool, int32_t *n_copied, void *ws,
+                           size_t ws_bytes, int32_t *dev_err, void *stream) {
     E0_REQUIRE(dims && store && pool, E0_ERR_INVALID_ARG);
     const int d = dims->d_model, f = dims->d_ff, E = dims->n_experts, K = dims->top_k;
     E0_REQUIRE(L >= 0 && B >= 1 && S >= 1 && K >= 1 && E >= 1, E0_ERR_INVALID_ARG);
@@ -313,7 +346,7 @@ extern "C" e0_status e0_slot_update(const e0_moe_dims *dims, int32_t L, int32_t 
     char *wsb = static_cast<char *>(ws);
     SlotArgs a{L, B * K, E, S, next_idx, cur_idx, slot_of, expert_of, n_copied, dev_err,
                reinterpret_cast<int32_t *>(wsb + lay.ncopy), reinterpret_cast<int32_t *>(wsb + lay.cslot),
-               reinterpret_cast<int32_t *>(wsb + lay.cexp), lay.maxc};
+               reinterpret_cast<int32_t *>(wsb + lay.cexp), lay.maxc, last_use, step};
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipLaunchKernelGGL(slot_plan_kernel, dim3(L), dim3(kThreads), 0, st, a);
     e0_status s = e0_launch_status();
@@ -331,4 +364,26 @@ extern "C" e0_status e0_slot_update(const e0_moe_dims *dims, int32_t L, int32_t 
     else
         hipLaunchKernelGGL(slot_copy_kernel, dim3(L, lay.maxc, (unsigned)chunks), dim3(kThreads), 0, st, c);
     return e0_launch_status();
+}
+
+}  // namespace
+
+extern "C" e0_status e0_slot_update(const e0_moe_dims *dims, int32_t L, int32_t B, int32_t S,
+                                    const int32_t *next_idx, const int32_t *cur_idx, int32_t *slot_of,
+                                    int32_t *expert_of, const e0_stack *store, const e0_stack *pool,
+                                    int32_t *n_copied, void *ws, size_t ws_bytes, int32_t *dev_err, void *stream) {
+    e0_clear_stale_error();
+    return slot_update_impl(dims, L, B, S, next_idx, cur_idx, slot_of, expert_of, nullptr, 0, store, pool, n_copied,
+                            ws, ws_bytes, dev_err, stream);
+}
+
+extern "C" e0_status e0_slot_update_lru(const e0_moe_dims *dims, int32_t L, int32_t B, int32_t S,
+                                        const int32_t *next_idx, const int32_t *cur_idx, int32_t *slot_of,
+                                        int32_t *expert_of, int32_t *last_use, int32_t step, const e0_stack *store,
+                                        const e0_stack *pool, int32_t *n_copied, void *ws, size_t ws_bytes,
+                                        int32_t *dev_err, void *stream) {
+    e0_clear_stale_error();
+    E0_REQUIRE(last_use && step >= 0, E0_ERR_INVALID_ARG);
+    return slot_update_impl(dims, L, B, S, next_idx, cur_idx, slot_of, expert_of, last_use, step, store, pool,
+                            n_copied, ws, ws_bytes, dev_err, stream);
 }
