@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--host-store", action="store_true",
                     help="keep the expert store in pinned host memory (the HBM slot pool as its cache; the slot "
                          "update pulls changed experts over the host link)")
+    ap.add_argument("--hot-slots", type=int, default=0, metavar="S",
+                    help="staged workloads: S slots per layer kept as a least-recently-used hot set of the store "
+                         "(e0_slot_update_lru) instead of the workload's 2K slots with the lowest-slot rule")
     ap.add_argument("--cpu-steps", type=int, default=0, help="oracle sample size (0 = auto)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference kernel for the "
@@ -120,7 +123,7 @@ def bench_decode(args, cfg, n_in, chain=False):
     from int4_gather_swiglu_amd.pipeline import StagedPipeline
 
     dev = torch.device("cuda:0")
-    L, B, K, Ex, S, d, f = cfg.L, cfg.B, cfg.K, cfg.E, cfg.S, cfg.d, cfg.f
+    L, B, K, Ex, S, d, f = cfg.L, cfg.B, cfg.K, cfg.E, args.hot_slots or cfg.S, cfg.d, cfg.f
     bb = gen.bundle_bytes(d, f)
     # The full expert store filled on the GPU; per-step inputs drawn on the
     # host and resident in HBM before the timed region.
@@ -141,7 +144,8 @@ def bench_decode(args, cfg, n_in, chain=False):
         r_out = torch.empty((L, d), dtype=torch.float32, device=dev)
     dims = E.moe_dims(d, f, Ex, K)
     pipe = StagedPipeline(dims, L, B, S, E.stack_from_bundles(store, d, f, bb, Ex * bb),
-                          E.stack_from_bundles(pool, d, f, bb, S * bb), device=dev, side_stream=not args.no_overlap)
+                          E.stack_from_bundles(pool, d, f, bb, S * bb), device=dev, side_stream=not args.no_overlap,
+                          hot_set=bool(args.hot_slots))
     rp = E.route_params(cfg.mode, K, cfg.n_groups, cfg.topk_groups, cfg.scale, cfg.eps)
 
     def route(buf, t, on_side):
@@ -469,7 +473,7 @@ def bench_prerouted(args, cfg, n_in):
     from int4_gather_swiglu_amd.pipeline import PrerouterPipeline
 
     dev = torch.device("cuda:0")
-    L, K, Ex, S, d, f = cfg.L, cfg.K, cfg.E, cfg.S, cfg.d, cfg.f
+    L, K, Ex, S, d, f = cfg.L, cfg.K, cfg.E, args.hot_slots or cfg.S, cfg.d, cfg.f
     bb = gen.bundle_bytes(d, f)
 
     def f16(a):
@@ -493,7 +497,8 @@ def bench_prerouted(args, cfg, n_in):
     shared = E.shared_from_tensors(sh_store, d, cfg.shared_f, la, lb, cfg.lora_alpha_over_r)
     pipe = PrerouterPipeline(dims, L, 1, S, E.stack_from_bundles(store, d, f, bb, Ex * bb),
                              E.stack_from_bundles(pool, d, f, bb, S * bb), E.heads_from_tensors(*hd_t),
-                             E.route_params(0, K), shared=shared, device=dev, side_stream=not args.no_overlap)
+                             E.route_params(0, K), shared=shared, device=dev, side_stream=not args.no_overlap,
+                             hot_set=bool(args.hot_slots))
     R = torch.zeros((3, L + 1, 1, K), dtype=torch.int32, device=dev)
     Wt = torch.full((3, L + 1, 1, K), 1.0 / K, dtype=torch.float32, device=dev)
     R[0, 0, 0] = owner0[0]
@@ -645,6 +650,10 @@ def main():
     out.update(res)
     if wl not in ("prefill35b", "merge35b"):
         out["config"]["expert_store"] = "pinned host memory" if args.host_store else "HBM"
+        if args.hot_slots:
+            out["config"]["slots"] = args.hot_slots
+            out["config"]["workload"] += (f", {args.hot_slots} slots per layer kept as a least-recently-used hot set "
+                                          "(e0_slot_update_lru)")
         if args.host_store:
             out["config"]["workload"] += ", expert store in pinned host memory (HBM slots as its cache)"
     if "roofline" in out:

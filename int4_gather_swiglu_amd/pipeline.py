@@ -30,14 +30,19 @@ from . import _lib as E
 
 class StagedPipeline:
     def __init__(self, dims: E.MoeDims, L: int, B: int, S: int, store: E.Stack, pool: E.Stack,
-                 shared: E.Shared | None = None, device="cuda", side_stream: bool = True):
+                 shared: E.Shared | None = None, device="cuda", side_stream: bool = True, hot_set: bool = False):
+        """hot_set: keep the S slots per layer as a least-recently-used hot set of
+        the store (e0_slot_update_lru) instead of the lowest-free-slot rule."""
         self.dims, self.L, self.B, self.S = dims, L, B, S
+        self.hot_set = hot_set
+        self.step = 0
         self.store, self.pool, self.shared = store, pool, shared
         K, Ex = dims.top_k, dims.n_experts
         dev = torch.device(device)
         self.dev = dev
         self.slot_of = torch.full((L, Ex), -1, dtype=torch.int32, device=dev)
         self.expert_of = torch.full((L, S), -1, dtype=torch.int32, device=dev)
+        self.last_use = torch.full((L, S), -1, dtype=torch.int32, device=dev)
         self.idx = torch.zeros((2, L, B, K), dtype=torch.int32, device=dev)
         self.w = torch.zeros((2, L, B, K), dtype=torch.float32, device=dev)
         self.n_copied = torch.zeros((L,), dtype=torch.int32, device=dev)
@@ -72,8 +77,14 @@ class StagedPipeline:
         """Slot update for routing ids `nxt` [L][B][K], protecting `cur` (or None)."""
         if after_main:
             self.side_after_main()
-        E.e0_slot_update(self.dims, self.L, self.B, self.S, nxt, cur, self.slot_of, self.expert_of, self.store,
-                         self.pool, self.n_copied, self.ws_slot, self.err, stream=self.side)
+        if self.hot_set:
+            E.e0_slot_update_lru(self.dims, self.L, self.B, self.S, nxt, cur, self.slot_of, self.expert_of,
+                                 self.last_use, self.step, self.store, self.pool, self.n_copied, self.ws_slot,
+                                 self.err, stream=self.side)
+            self.step += 1
+        else:
+            E.e0_slot_update(self.dims, self.L, self.B, self.S, nxt, cur, self.slot_of, self.expert_of, self.store,
+                             self.pool, self.n_copied, self.ws_slot, self.err, stream=self.side)
         self.ev_updated.record(self.side)
 
     def update(self, nxt: int, cur: int | None, after_main: bool = True):
@@ -113,8 +124,8 @@ class PrerouterPipeline(StagedPipeline):
     R[t+1][j+1]."""
 
     def __init__(self, dims, L, B, S, store, pool, heads: E.PrerouterHeads, route: E.RouteParams,
-                 shared=None, device="cuda", side_stream: bool = True):
-        super().__init__(dims, L, B, S, store, pool, shared, device, side_stream)
+                 shared=None, device="cuda", side_stream: bool = True, hot_set: bool = False):
+        super().__init__(dims, L, B, S, store, pool, shared, device, side_stream, hot_set)
         self.heads, self.route = heads, route
         hd = E.moe_dims(dims.d_model, heads.hidden, dims.n_experts, dims.top_k)
         self.ws_pre = torch.empty(E.workspace_bytes(E.E0_OP_PREROUTER, hd, L, B), dtype=torch.uint8, device=self.dev)
