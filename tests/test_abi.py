@@ -155,6 +155,21 @@ def test_lora_merge_validation():
     assert call(16, 128, F, F, F, F, F, 16, C.c_float(2.0), F, H, I, None) == E.E0_ERR_INVALID_ARG
 
 
+def test_slot_update_lru_validation():
+    L = E.lib()
+    st = _stack()
+    dims = E.moe_dims(2048, 512, 256, 4)
+    F = C.c_void_p(FAKE)
+    # null last_use, negative step: refused before anything else is read
+    assert L.e0_slot_update_lru(C.byref(dims), 1, 1, 8, F, None, F, F, None, 0, C.byref(st), C.byref(st), None, F,
+                                1 << 20, F, None) == E.E0_ERR_INVALID_ARG
+    assert L.e0_slot_update_lru(C.byref(dims), 1, 1, 8, F, None, F, F, F, -1, C.byref(st), C.byref(st), None, F,
+                                1 << 20, F, None) == E.E0_ERR_INVALID_ARG
+    # the plain update's checks apply too (S above the limit)
+    assert L.e0_slot_update_lru(C.byref(dims), 1, 1, 5000, F, None, F, F, F, 0, C.byref(st), C.byref(st), None, F,
+                                1 << 20, F, None) == E.E0_ERR_CAPACITY
+
+
 def test_binding_has_no_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(E, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(E, "_LIB", None)
