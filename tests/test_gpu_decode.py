@@ -37,7 +37,7 @@ def _replay_tables(cfg, L, S, routes):
     return out
 
 
-def _run_steps(cfg, L, steps, S, logits_fn, x_fn, overlap=True):
+def _run_steps(cfg, L, steps, S, logits_fn, x_fn, overlap=True, hot_set=False):
     """Route -> slot update -> decode for `steps` steps; returns per-step
     (idx, w, y, slot_of, expert_of) on the host plus the device store/pool."""
     from int4_gather_swiglu_amd.pipeline import StagedPipeline
@@ -47,7 +47,7 @@ def _run_steps(cfg, L, steps, S, logits_fn, x_fn, overlap=True):
     pool = U.zeros((L, S, bb), "uint8")
     st_store, st_pool = _stacks(store, pool, cfg)
     dims = E().moe_dims(cfg.d, cfg.f, cfg.E, cfg.K)
-    pipe = StagedPipeline(dims, L, cfg.B, S, st_store, st_pool, side_stream=overlap)
+    pipe = StagedPipeline(dims, L, cfg.B, S, st_store, st_pool, side_stream=overlap, hot_set=hot_set)
     p = E().route_params(cfg.mode, cfg.K, cfg.n_groups, cfg.topk_groups, cfg.scale, cfg.eps)
     lgs = [U.f16(logits_fn(t)) for t in range(steps)]
     xs = [U.f16(x_fn(t)) for t in range(steps)]
@@ -64,7 +64,8 @@ def _run_steps(cfg, L, steps, S, logits_fn, x_fn, overlap=True):
         T.cuda.current_stream().synchronize()
         pipe.side.synchronize()
         rec = dict(idx=pipe.idx[t % 2].cpu().numpy(), w=pipe.w[t % 2].cpu().numpy(),
-                   slot_of=pipe.slot_of.cpu().numpy(), expert_of=pipe.expert_of.cpu().numpy())
+                   slot_of=pipe.slot_of.cpu().numpy(), expert_of=pipe.expert_of.cpu().numpy(),
+                   last_use=pipe.last_use.cpu().numpy())
         if t + 1 < steps:
             pipe.update((t + 1) % 2, t % 2)
         pipe.decode(t % 2, xs[t], ys[t])
@@ -104,6 +105,30 @@ def test_tiny_decode_steps(B):
     for t in range(steps):
         assert np.array_equal(recs[t]["slot_of"], tables[t][0]), t
         assert np.array_equal(recs[t]["expert_of"], tables[t][1]), t
+        for l in range(L):
+            _check_layer(cfg, l, recs[t], W.activations(cfg, t, l))
+
+
+def test_hot_set_decode_steps():
+    # The pool as a least-recently-used hot set (S between one step's need and
+    # the store): tables step by step as the oracle's rule, and every layer's
+    # output exact whatever the policy evicted.
+    from oracle import lru as R
+    cfg = W.scaled(W.TINY, B=2, L=2, E=32, S=20)
+    L, steps, S = cfg.L, 6, 20
+    recs, store, pool = _run_steps(cfg, L, steps, S, lambda t: np.stack([W.given_logits(cfg, t, l) for l in range(L)]),
+                                   lambda t: np.stack([W.activations(cfg, t, l) for l in range(L)]), hot_set=True)
+    so = [[-1] * cfg.E for _ in range(L)]
+    eo = [[-1] * S for _ in range(L)]
+    lu = [[-1] * S for _ in range(L)]
+    for t in range(steps):
+        for l in range(L):
+            prev = recs[t - 1]["idx"][l].ravel().tolist() if t > 0 else []
+            _, bad = R.slot_update_lru(cfg.E, S, recs[t]["idx"][l].ravel().tolist(), prev, so[l], eo[l], lu[l], t)
+            assert not bad
+        assert np.array_equal(recs[t]["slot_of"], np.array(so)), t
+        assert np.array_equal(recs[t]["expert_of"], np.array(eo)), t
+        assert np.array_equal(recs[t]["last_use"], np.array(lu)), t
         for l in range(L):
             _check_layer(cfg, l, recs[t], W.activations(cfg, t, l))
 
