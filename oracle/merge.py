@@ -10,12 +10,21 @@ section 3.3): retention = 1 - |U - M| / |U - B| with U the unmerged, M the
 merged and B the base weights; xyznot.com FAQ on why the recovery LoRA stays
 unmerged: deltas of RMS about 1e-3 sit below one 4-bit step, so merging and
 requantising erases most of them. The pages do not print the requantisation
-rule; this follows the plainest reading of the stacks' affine format:
-scale = (max - min) / 15, bias = min, codes rounded half to even and clamped
-to 0..15, scale and bias stored as fp16. The merged codes are an integer
-decision taken from fp32 values, so it is taken in fp32 here, each operation
-rounded to nearest on its own (numpy float32 arithmetic), in the order the
-kernel uses: w = s*q + b; t = sum_k B[i,k]*A[k,c] in k order; w' = w + a*t.
+rule; this follows the plainest reading of the stacks' affine format, written
+out from its definition in fp64:
+
+    w'  = s*q + b + alpha * sum_k B[i,k] * A[k,c]           (fp64)
+    s'  = fp16((max w' - min w') / 15)    per (row, 64-column group)
+    b'  = fp16(min w')
+    q'  = clamp(round_half_even((w' - b') / s'), 0, 15)     (0 where s' = 0)
+
+s*q + b and every B*A product of fp16 values are exact in fp64; the quotient
+is taken in fp64 against the fp16-rounded s' and b'. A GPU that computes w'
+and the quotient in fp32 takes the same integer decision except where the
+fp64 quotient lies within its rounding error of a half-integer, and the same
+fp16 scale except where (max - min) / 15 lies that close to an fp16 rounding
+boundary: ``boundary_distance`` and ``scale_boundary_distance`` give what a
+parity check needs to allow exactly those cases.
 
 Matrices are (q uint32 [rows][cols/8], s uint16 [rows][cols/64], b uint16
 [rows][cols/64]) with fp16 bit patterns in s and b (the oracle's format);
@@ -42,65 +51,89 @@ def pack(c: np.ndarray) -> np.ndarray:
     return np.bitwise_or.reduce(c << (np.arange(8, dtype=np.uint32) * 4)[None, None, :], axis=2).astype(np.uint32)
 
 
-def merged_weights_f32(q, s, b, lora_b, lora_a, alpha_over_r) -> np.ndarray:
-    """w' = (s*q + b) + alpha * sum_k B[i,k] A[k,c], fp32, every step rounded."""
-    rows = q.shape[0]
-    cols = q.shape[1] * 8
-    s32 = np.asarray(s, dtype=np.uint16).view(np.float16).astype(np.float32)
-    b32 = np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
-    cq = codes(q, cols).astype(np.float32)
-    se = np.repeat(s32, GROUP, axis=1)
-    be = np.repeat(b32, GROUP, axis=1)
-    w = (se * cq).astype(np.float32)
-    w = (w + be).astype(np.float32)
-    B = np.asarray(lora_b, dtype=np.uint16).view(np.float16).astype(np.float32).reshape(rows, -1)
-    A = np.asarray(lora_a, dtype=np.uint16).view(np.float16).astype(np.float32).reshape(-1, cols)
-    t = np.zeros((rows, cols), dtype=np.float32)
-    for k in range(A.shape[0]):
-        t = (t + (B[:, k:k + 1] * A[k:k + 1, :]).astype(np.float32)).astype(np.float32)
-    a = np.float32(alpha_over_r)
-    return (w + (a * t).astype(np.float32)).astype(np.float32)
-
-
-def requantize(w: np.ndarray):
-    """Per (row, 64-column group) of fp32 w: s' = fp16((max-min)/15), b' = fp16(min),
-    q' = clamp(rint((w - b') / s'), 0, 15) (0 where s' is 0). Returns (q, s, b) in
-    the oracle's format."""
-    rows, cols = w.shape
-    g = w.reshape(rows, cols // GROUP, GROUP)
-    hi = g.max(axis=2)
-    lo = g.min(axis=2)
-    s32 = ((hi - lo).astype(np.float32) / np.float32(15.0)).astype(np.float32)
-    s16 = s32.astype(np.float16)
-    b16 = lo.astype(np.float16)
-    sf = s16.astype(np.float32)[:, :, None]
-    bf = b16.astype(np.float32)[:, :, None]
-    with np.errstate(divide="ignore", invalid="ignore"):
-        v = np.rint(((g - bf).astype(np.float32) / np.where(sf == 0, np.float32(1), sf)).astype(np.float32))
-    v = np.clip(v, 0, 15)
-    v = np.where(sf == 0, 0, v).astype(np.uint32).reshape(rows, cols)
-    return pack(v), s16.view(np.uint16).copy(), b16.view(np.uint16).copy()
-
-
-def merge_requant(q, s, b, lora_b, lora_a, alpha_over_r):
-    """The merged matrix: requantize(merged_weights_f32(...))."""
-    return requantize(merged_weights_f32(q, s, b, lora_b, lora_a, alpha_over_r))
+def _f16(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
 
 
 def dequant64(q, s, b) -> np.ndarray:
     """s*q + b in fp64 (exact for fp16 s, b and 4-bit q)."""
     cols = q.shape[1] * 8
-    s64 = np.asarray(s, dtype=np.uint16).view(np.float16).astype(np.float64)
-    b64 = np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float64)
-    return np.repeat(s64, GROUP, axis=1) * codes(q, cols) + np.repeat(b64, GROUP, axis=1)
+    return np.repeat(_f16(s), GROUP, axis=1) * codes(q, cols) + np.repeat(_f16(b), GROUP, axis=1)
+
+
+def merged_weights(q, s, b, lora_b, lora_a, alpha_over_r) -> np.ndarray:
+    """w' = (s*q + b) + alpha * sum_k B[i,k] A[k,c] in fp64, the rank sum written
+    out term by term (each term is exact in fp64)."""
+    w = dequant64(q, s, b)
+    rows, cols = w.shape
+    B = _f16(lora_b).reshape(rows, -1)
+    A = _f16(lora_a).reshape(-1, cols)
+    t = np.zeros((rows, cols), dtype=np.float64)
+    for k in range(A.shape[0]):
+        t += B[:, k:k + 1] * A[k:k + 1, :]
+    return w + float(alpha_over_r) * t
+
+
+def group_scale_bias(w: np.ndarray):
+    """Per (row, group) of fp64 w: (range / 15 in fp64, s' fp16, b' fp16)."""
+    rows, cols = w.shape
+    g = w.reshape(rows, cols // GROUP, GROUP)
+    exact = (g.max(axis=2) - g.min(axis=2)) / 15.0
+    return exact, exact.astype(np.float16), g.min(axis=2).astype(np.float16)
+
+
+def quotients(w: np.ndarray, s16: np.ndarray, b16: np.ndarray) -> np.ndarray:
+    """(w' - b') / s' in fp64 for every weight, given per-group fp16 s', b'
+    (float16 arrays [rows][groups]); NaN where s' = 0."""
+    rows, cols = w.shape
+    sf = np.repeat(np.asarray(s16, dtype=np.float16).astype(np.float64), GROUP, axis=1)
+    bf = np.repeat(np.asarray(b16, dtype=np.float16).astype(np.float64), GROUP, axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.where(sf == 0, np.nan, (w - bf) / np.where(sf == 0, 1.0, sf))
+
+
+def codes_from_quotients(u: np.ndarray) -> np.ndarray:
+    """clamp(round_half_even(u), 0, 15), 0 where u is NaN (a constant group)."""
+    v = np.clip(np.rint(np.nan_to_num(u, nan=0.0)), 0, 15)
+    return v.astype(np.uint32)
+
+
+def requantize(w: np.ndarray):
+    """Min/max affine requantisation of fp64 w' (see the module docstring).
+    Returns (q, s, b) in the oracle's format."""
+    _, s16, b16 = group_scale_bias(w)
+    q = codes_from_quotients(quotients(w, s16, b16))
+    return pack(q), s16.view(np.uint16).copy(), b16.view(np.uint16).copy()
+
+
+def merge_requant(q, s, b, lora_b, lora_a, alpha_over_r):
+    """The merged matrix: requantize(merged_weights(...))."""
+    return requantize(merged_weights(q, s, b, lora_b, lora_a, alpha_over_r))
+
+
+def boundary_distance(u: np.ndarray) -> np.ndarray:
+    """Distance of each quotient to the nearest half-integer (where rounding
+    flips); +inf where u is NaN."""
+    return np.where(np.isnan(u), np.inf, np.abs(np.abs(u - np.floor(u)) - 0.5))
+
+
+def scale_boundary_distance(exact: np.ndarray) -> np.ndarray:
+    """Relative distance of range / 15 to the nearest point where its fp16
+    rounding flips (the midpoint between two adjacent fp16 values)."""
+    h = exact.astype(np.float16)
+    lo = np.where(h.astype(np.float64) <= exact, h, np.nextafter(h, np.float16(-np.inf)))
+    hi = np.nextafter(lo, np.float16(np.inf))
+    mid = (lo.astype(np.float64) + hi.astype(np.float64)) / 2.0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.where(exact == 0, np.inf, np.abs(exact - mid) / np.abs(exact))
 
 
 def retention(base, merged, lora_b, lora_a, alpha_over_r) -> float:
     """1 - |U - M| / |U - B| (Frobenius norms, fp64): B the base weights, U = B +
     alpha * lora_b @ lora_a (the unmerged delta, exact), M the merged matrix."""
     Bw = dequant64(*base)
-    Bm = np.asarray(lora_b, dtype=np.uint16).view(np.float16).astype(np.float64).reshape(Bw.shape[0], -1)
-    Am = np.asarray(lora_a, dtype=np.uint16).view(np.float16).astype(np.float64).reshape(-1, Bw.shape[1])
+    Bm = _f16(lora_b).reshape(Bw.shape[0], -1)
+    Am = _f16(lora_a).reshape(-1, Bw.shape[1])
     U = Bw + float(alpha_over_r) * (Bm @ Am)
     M = dequant64(*merged)
     return float(1.0 - np.linalg.norm(U - M) / np.linalg.norm(U - Bw))

@@ -1,13 +1,18 @@
 """Pins of the merged-LoRA oracle (oracle/merge.py) against what the format
 and the arithmetic fix, independent of its own code:
 - requantising a group that already lies on a 16-level grid (zero delta)
-  gives back its codes (the scale rule is range / 15, not / 16);
+  gives back its codes, scale and bias exactly (the scale rule is range / 15,
+  not / 16);
+- quotients that fall exactly on a half-integer round to the even code;
 - a constant group has scale 0, codes 0 and its value as bias;
 - the group's least value takes code 0 and its largest code 15;
 - every requantised weight is within half a step (plus the fp16 rounding of
   scale and bias) of the merged fp32 weight;
-- the fp32 merged weights agree with base + alpha * B @ A computed in fp64 by
-  numpy's matrix product (a transposed or mis-indexed operand fails);
+- the merged weights (rank sum written term by term) agree with base +
+  alpha * B @ A from numpy's matrix product (a transposed or mis-indexed
+  operand fails);
+- the boundary helpers a GPU parity check uses give the distances of known
+  points to the nearest rounding flip;
 - retention (jaehun.me review, the paragraph on not merging; xyznot.com FAQ on
   the unmerged recovery LoRA): a delta far below one 4-bit step is mostly
   erased, one far above it mostly kept, an exact whole-step shift kept."""
@@ -38,9 +43,7 @@ def test_zero_delta_on_full_grid_keeps_codes():
     za = np.zeros((4, cols), dtype=np.uint16)
     q2, s2, b2 = M.merge_requant(q, s, b, zb, za, 2.0)
     assert np.array_equal(q2, q)
-    s_old = s.view(np.float16).astype(np.float64)
-    s_new = s2.view(np.float16).astype(np.float64)
-    assert np.all(np.abs(s_new - s_old) <= np.abs(s_old) * 2.0 ** -10)  # at most one fp16 ulp
+    assert np.array_equal(s2, s)  # 15 s / 15 = s exactly in fp64
     assert np.array_equal(b2, b)
 
 
@@ -60,7 +63,7 @@ def test_extremes_take_codes_0_and_15_and_error_within_half_step():
     rows, cols, r = 32, 256, 8
     q, s, b = _base(rows, cols)
     lb, la = _lora(rows, cols, r, 0.05)
-    w = M.merged_weights_f32(q, s, b, lb, la, 2.0)
+    w = M.merged_weights(q, s, b, lb, la, 2.0)
     q2, s2, b2 = M.requantize(w)
     c = M.codes(q2, cols).reshape(rows, cols // 64, 64)
     g = w.reshape(rows, cols // 64, 64)
@@ -78,9 +81,13 @@ def test_merged_weights_match_fp64_matrix_product():
     rows, cols, r = 24, 192, 5
     q, s, b = _base(rows, cols)
     lb, la = _lora(rows, cols, r, 0.1)
-    w = M.merged_weights_f32(q, s, b, lb, la, 2.0).astype(np.float64)
+    w = M.merged_weights(q, s, b, lb, la, 2.0)
     ref = M.dequant64(q, s, b) + 2.0 * (lb.view(np.float16).astype(np.float64) @ la.view(np.float16).astype(np.float64))
-    assert np.max(np.abs(w - ref)) <= 1e-6 * max(1.0, np.max(np.abs(ref)))
+    assert np.max(np.abs(w - ref)) <= 1e-13 * max(1.0, np.max(np.abs(ref)))
+    # a transposed operand (B^T-shaped use of A) is caught
+    bad = M.dequant64(q, s, b) + 2.0 * (lb.view(np.float16).astype(np.float64)
+                                        @ np.roll(la.view(np.float16).astype(np.float64), 1, axis=1))
+    assert np.max(np.abs(w - bad)) > 1e-3
 
 
 def test_retention_small_delta_erased_large_delta_kept():
@@ -109,3 +116,36 @@ def test_retention_of_whole_step_shift_is_one():
     assert np.array_equal(merged[0], q) and np.array_equal(merged[1], s)
     assert np.all(merged[2].view(np.float16) == np.float16(-0.125 + 0.015625))
     assert abs(M.retention((q, s, b), merged, lb, la, 2.0) - 1.0) < 1e-12
+
+
+def test_half_integer_quotients_round_to_even():
+    # One group, scale 2^-6 and bias 0 exactly (least 0, largest 15 * 2^-6), the
+    # other weights placed so that (w - b) / s is k + 1/2 exactly for k = 0..13:
+    # round half to even gives 0, 2, 2, 4, 4, ..., 14 (a half-up rule would give
+    # 1, 2, 3, ...; a truncation 0, 1, 2, ...).
+    step = 2.0 ** -6
+    w = np.zeros((1, 64))
+    w[0, 1] = 15 * step
+    halves = np.arange(14) + 0.5
+    w[0, 2:16] = halves * step
+    w[0, 16:] = 7 * step
+    q, s, b = M.requantize(w)
+    assert s.view(np.float16)[0, 0] == np.float16(step) and b.view(np.float16)[0, 0] == 0
+    c = M.codes(q, 64)[0]
+    assert c[0] == 0 and c[1] == 15 and np.all(c[16:] == 7)
+    assert c[2:16].tolist() == [0, 2, 2, 4, 4, 6, 6, 8, 8, 10, 10, 12, 12, 14]
+
+
+def test_boundary_helpers_on_known_points():
+    u = np.array([[0.5, 2.25, 3.0, 14.4999, np.nan]])
+    d = M.boundary_distance(u)
+    assert d[0, 0] == 0.0 and d[0, 1] == 0.25 and d[0, 2] == 0.5
+    assert abs(d[0, 3] - 1e-4) < 1e-12 and np.isinf(d[0, 4])
+    # fp16 values 1 and 1 + 2^-10: their midpoint 1 + 2^-11 is where rounding flips
+    one = 1.0
+    mid = 1.0 + 2.0 ** -11
+    e = np.array([one, mid, mid * (1 + 1e-6), 0.0])
+    sd = M.scale_boundary_distance(e)
+    assert abs(sd[0] - 2.0 ** -11) < 1e-15
+    assert sd[1] == 0.0
+    assert abs(sd[2] - 1e-6) < 1e-9 and np.isinf(sd[3])
