@@ -262,3 +262,37 @@ def chain_decode(pools: Experts, S, slot_of, E, d, f, r0, g, eps, idx, w):
     err = lib().orc_chain_decode(pools.ptr, S, _p(so), L, E, d, f, K, _p(r0), _p(g), C.c_double(eps), _p(idx),
                                  _p(w), _p(y), _p(r_out))
     return y, r_out, err
+
+
+def moe_by_expert(expert_fn, E, d, f, x, idx, w):
+    """One MoE layer over T tokens with each active expert dequantised once
+    (orc_dequant, fp64) and applied to all of its tokens as fp64 matrix
+    products (numpy): the exact ordering of the combine (jaehun.me review,
+    report 3.1, the whole-layer path) at sizes where the per-(token, k) C loop
+    is too slow.
+
+    expert_fn(e) -> [(q, s, b)] * 3 (gate [f][d], up [f][d], down [d][f]);
+    x fp16 [T][d]; idx int32 [T][K]; w [T][K]. Pairs with an id outside
+    0..E-1 contribute nothing. y [T][d] fp64 = sum over k, in k order, of
+    w[t][k] * down(silu(gate x_t) * up x_t)."""
+    x64 = np.asarray(x, dtype=np.float16).astype(np.float64)
+    idx = np.asarray(idx, dtype=np.int64)
+    w = np.asarray(w, dtype=np.float64)
+    T, K = idx.shape
+    yk = np.zeros((T, K, d), dtype=np.float64)
+    for e in np.unique(idx):
+        if e < 0 or e >= E:
+            continue
+        (gq, gs, gb), (uq, us, ub), (dq, ds, db) = expert_fn(int(e))
+        G = dequant(gq, gs, gb, f, d)
+        Uw = dequant(uq, us, ub, f, d)
+        D = dequant(dq, ds, db, d, f)
+        t, k = np.nonzero(idx == e)
+        X = x64[t]
+        a = X @ G.T
+        h = a / (1.0 + np.exp(-a)) * (X @ Uw.T)
+        yk[t, k] = w[t, k][:, None] * (h @ D.T)
+    y = yk[:, 0].copy()
+    for k in range(1, K):
+        y += yk[:, k]
+    return y

@@ -61,3 +61,23 @@ def rel_l2(got, ref) -> float:
 
 def bytes_of(t):
     return t.numel() * t.element_size()
+
+
+def elem_err(got, ref) -> float:
+    """Largest per-row ratio max_i |got - ref| / max_i |ref| (rows = last axis)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    g2 = got.reshape(-1, got.shape[-1])
+    r2 = ref.reshape(-1, ref.shape[-1])
+    num = np.max(np.abs(g2 - r2), axis=1)
+    den = np.maximum(np.max(np.abs(r2), axis=1), 1e-300)
+    return float(np.max(num / den))
+
+
+def assert_close(got, ref, rel_l2_tol: float, elem_tol: float, what: str = ""):
+    """Both bars: whole-array rel-L2 and, per row, the largest element error
+    against the row's largest reference value (a sparse indexing mistake that
+    the norm would average away fails the second). Returns (rel_l2, elem)."""
+    r, e = rel_l2(got, ref), elem_err(got, ref)
+    assert r <= rel_l2_tol and e <= elem_tol, (what, r, e)
+    return r, e

@@ -10,6 +10,7 @@ from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
+ELEM = 1e-4  # per token: max |y - ref| / max |ref| (fp32 accumulation of exact weights: ~1e-6)
 
 
 def E():
@@ -85,8 +86,7 @@ def _check_layer(cfg, layer, rec, x, tol=TOL):
     lst = [experts.get(e, experts[ids[0]]) for e in range(cfg.E)]
     ref, err = oracle.moe_exact(oracle.Experts(lst), cfg.d, cfg.f, x, rec["idx"][layer], rec["w"][layer].astype(np.float64))
     assert err == 0
-    r = U.rel_l2(rec["y"][layer], ref)
-    assert r <= tol, (cfg.name, layer, r)
+    r, _ = U.assert_close(rec["y"][layer], ref, tol, ELEM, (cfg.name, layer))
     return r
 
 

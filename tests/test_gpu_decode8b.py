@@ -12,6 +12,7 @@ from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
+ELEM = 1e-4  # per token: max |y - ref| / max |ref|
 DELTA = 1e-3
 
 
@@ -84,7 +85,7 @@ def test_decode8b_steps(cfg):
             lst = [mats.get(e, mats[ids[0]]) for e in range(cfg.E)]
             ref, _ = oracle.moe_exact(oracle.Experts(lst), cfg.d, cfg.f, xs_h[t][l][tok], recs[t]["idx"][l][tok],
                                       recs[t]["w"][l][tok].astype(np.float64))
-            rs.append(U.rel_l2(y[l][tok], ref))
+            rs.append(U.assert_close(y[l][tok], ref, TOL, ELEM, (t, l))[0])
     uniq = [len(set(recs[0]["idx"][l].ravel().tolist())) for l in range(L)]
     print(cfg.name, "rel-L2", max(rs), "unique experts/layer", min(uniq), max(uniq))
     assert max(rs) <= TOL

@@ -14,6 +14,7 @@ from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
+ELEM = 1e-4  # per token: max |y - ref| / max |ref|
 
 # token -> its three routed experts; 99 is out of range, 13 has no slot
 IDX = [[2, 5, 9], [2, 5, 13], [2, 7, 9], [2, 99, 5], [2, 11, 1], [2, 5, 0], [4, 7, 9]]
@@ -54,5 +55,4 @@ def test_batched_decode_ragged_pairs_and_skips():
     assert rerr == 3
     got = y.cpu().numpy()[0]
     for t in range(B):
-        r = U.rel_l2(got[t], ref[t])
-        assert r <= TOL, (t, r)
+        U.assert_close(got[t], ref[t], TOL, ELEM, t)

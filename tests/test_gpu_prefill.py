@@ -1,7 +1,11 @@
 """GPU parity: sorted whole-layer prefill (sort by expert, MFMA grouped GEMM,
-weighted combine) against the fp64 oracle, rel-L2 <= 1e-3. fp16 MFMA
-operands (x exact; weights and the SwiGLU hidden rounded to fp16) put the
-expected error near 3e-4."""
+weighted combine) against the fp64 oracle, rel-L2 <= 1e-3 and, per token,
+max |y - ref| <= ELEM * max |ref|. fp16 MFMA operands (x exact; weights and
+the SwiGLU hidden rounded to fp16, each within 2^-11 relative) put the
+expected rel-L2 near 4e-4; the largest element error of a row is then about
+as large relative to the row's largest value, and ELEM = 3e-3 leaves a
+margin while a wrong 32-row block or column block (an O(1) error on a few
+elements) still fails."""
 import numpy as np
 import pytest
 
@@ -11,6 +15,7 @@ from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
+ELEM = 3e-3
 
 
 def E():
@@ -55,9 +60,7 @@ def test_tiny_prefill_all_tokens():
     y, err = _prefill(cfg, store, x, idx, w.astype(np.float32))
     assert err == 0
     ref = _oracle(cfg, 0, x, idx, w.astype(np.float32), np.arange(cfg.B))
-    r = U.rel_l2(y, ref)
-    print("tiny prefill rel-L2", r)
-    assert r <= TOL
+    print("tiny prefill rel-L2, elem", U.assert_close(y, ref, TOL, ELEM))
 
 
 @pytest.mark.parametrize("T", [1, 5, 128, 300])
@@ -69,7 +72,7 @@ def test_tiny_prefill_ragged_and_single_token(T):
     y, err = _prefill(cfg, store, x, idx, w.astype(np.float32))
     assert err == 0
     tok = np.unique(np.linspace(0, T - 1, min(T, 24)).astype(int))
-    assert U.rel_l2(y[tok], _oracle(cfg, 0, x, idx, w.astype(np.float32), tok)) <= TOL
+    U.assert_close(y[tok], _oracle(cfg, 0, x, idx, w.astype(np.float32), tok), TOL, ELEM)
 
 
 def test_prefill_one_expert_takes_every_token():
@@ -82,7 +85,7 @@ def test_prefill_one_expert_takes_every_token():
     y, err = _prefill(cfg, store, x, idx, w)
     assert err == 0
     tok = np.arange(0, cfg.B, 13)
-    assert U.rel_l2(y[tok], _oracle(cfg, 0, x, idx, w, tok)) <= TOL
+    U.assert_close(y[tok], _oracle(cfg, 0, x, idx, w, tok), TOL, ELEM)
 
 
 def test_prefill_bad_ids_flag_and_skip():
@@ -95,16 +98,31 @@ def test_prefill_bad_ids_flag_and_skip():
     w = w.astype(np.float32)
     y, err = _prefill(cfg, store, x, idx, w)
     assert err == E().E0_DEV_BAD_ID
-    assert U.rel_l2(y, _oracle(cfg, 0, x, idx, w, np.arange(cfg.B))) <= TOL
+    U.assert_close(y, _oracle(cfg, 0, x, idx, w, np.arange(cfg.B)), TOL, ELEM)
 
 
-def test_prefill35b_zipf_full_shape_sampled():
-    cfg = W.PREFILL35
-    T = cfg.B
+def _by_expert(cfg, x, idx, w):
+    """Every token at once: each active expert dequantised once, fp64 products."""
+    return oracle.moe_by_expert(lambda e: gen.expert(cfg.seed, 0, e, cfg.d, cfg.f), cfg.E, cfg.d, cfg.f, x, idx, w)
+
+
+def test_tiny_prefill_13k_pairs_every_token():
+    # T*K = 13,200 pairs (the pages' ~3.3k-token prompt at K = 4): more pairs
+    # than the sort loads in one batch, so its later batches run; every token
+    # compared.
+    cfg = W.scaled(W.TINY, B=3300)
     store = U.gpu_store(cfg, [0])[0]
-    x = W.activations(cfg, 0, 0)
-    lg16 = W.given_logits(cfg, 0, 0)
-    # routing on the GPU (as the bench does), checked against the oracle
+    x = W.activations(cfg, 4, 0)
+    idx, w = oracle.softmax_topk(W.given_logits(cfg, 4, 0).astype(np.float32), cfg.K)
+    w = w.astype(np.float32)
+    y, err = _prefill(cfg, store, x, idx, w)
+    assert err == 0
+    print("tiny T=3300 rel-L2, elem", U.assert_close(y, _by_expert(cfg, x, idx, w), TOL, ELEM))
+
+
+def _routed_on_gpu(cfg, lg16):
+    """Routing on the GPU (as the bench does), checked bit-exact against the oracle."""
+    T = cfg.B
     p = E().route_params(0, cfg.K)
     idx_d = U.empty((1, T, cfg.K), "int32")
     w_d = U.empty((1, T, cfg.K))
@@ -112,17 +130,25 @@ def test_prefill35b_zipf_full_shape_sampled():
     U.torch().cuda.synchronize()
     idx = idx_d.cpu().numpy()[0]
     w = w_d.cpu().numpy()[0]
-    ridx, rw = oracle.softmax_topk(lg16.astype(np.float32), cfg.K)
+    ridx, _ = oracle.softmax_topk(lg16.astype(np.float32), cfg.K)
     assert np.array_equal(idx, ridx)
+    return idx, w
+
+
+@pytest.mark.parametrize("T", [2048, 3300])
+def test_prefill35b_zipf_full_shape_every_token(T):
+    # The 35B-tier layer with Zipf(1.1) popularity at the workload's T = 2048
+    # and at the pages' prompt length (13,200 pairs): every token compared, so
+    # every M-tile of every active expert (heavy, mid and tail classes) and
+    # every column block is checked.
+    cfg = W.scaled(W.PREFILL35, B=T)
+    store = U.gpu_store(cfg, [0])[0]
+    x = W.activations(cfg, 0, 0)
+    idx, w = _routed_on_gpu(cfg, W.given_logits(cfg, 0, 0))
     counts = np.bincount(idx.ravel(), minlength=cfg.E)
     print("active experts", int((counts > 0).sum()), "top count", int(counts.max()),
           "experts < 16 rows", int(((counts > 0) & (counts < 16)).sum()))
     y, err = _prefill(cfg, store, x, idx, w)
     assert err == 0
-    top = int(np.argmax(counts))
-    tok_top = np.nonzero((idx == top).any(1))[0][:6]
-    tok_rare = [int(np.nonzero((idx == e).any(1))[0][0]) for e in np.nonzero((counts > 0) & (counts < 4))[0][:6]]
-    tok = np.unique(np.concatenate([tok_top, tok_rare, [0, T - 1]])).astype(int)
-    r = U.rel_l2(y[tok], _oracle(cfg, 0, x, idx, w, tok))
-    print("prefill35b rel-L2 on", len(tok), "tokens:", r)
-    assert r <= TOL
+    r, e = U.assert_close(y, _by_expert(cfg, x, idx, w), TOL, ELEM, f"prefill35b T={T}")
+    print(f"prefill35b T={T}: rel-L2 {r:.3g}, largest element error / row max {e:.3g}")

@@ -293,3 +293,22 @@ def test_decode_layers_threads_agree():
     a = oracle.decode_layers(P, S, np.stack(slot_of), cfg.E, cfg.d, cfg.f, np.stack(xs), np.stack(idxs), np.stack(ws), 1)
     b = oracle.decode_layers(P, S, np.stack(slot_of), cfg.E, cfg.d, cfg.f, np.stack(xs), np.stack(idxs), np.stack(ws), 3)
     assert a[1] == 0 and np.array_equal(a[0], b[0])
+
+
+def test_moe_by_expert_equals_per_pair_loop():
+    # The per-expert matrix-product form (used for full-size GPU parity) against
+    # the C oracle's per-(token, k) loop: same definition, different summation
+    # order, so equal to fp64 rounding. An out-of-range id contributes nothing
+    # in both.
+    cfg = W.scaled(W.TINY, B=37)
+    x = W.activations(cfg, 5, 0)
+    idx, w = oracle.softmax_topk(W.given_logits(cfg, 5, 0).astype(np.float32), cfg.K)
+    idx[3, 1] = cfg.E
+    w[3, 1] = 0.0
+    mats = [gen.expert(cfg.seed, 0, e, cfg.d, cfg.f) for e in range(cfg.E)]
+    ref, err = oracle.moe_exact(oracle.Experts(mats), cfg.d, cfg.f, x, idx, w)
+    got = oracle.moe_by_expert(lambda e: mats[e], cfg.E, cfg.d, cfg.f, x, idx, w)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+    # a swapped gate/up in the per-expert form is caught
+    swapped = oracle.moe_by_expert(lambda e: [mats[e][1], mats[e][0], mats[e][2]], cfg.E, cfg.d, cfg.f, x, idx, w)
+    assert np.linalg.norm(swapped - ref) / np.linalg.norm(ref) > 0.1
