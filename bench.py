@@ -68,9 +68,56 @@ def mean_ms(evs):
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
+def host_cpus():
+    """The host cores this process may run on."""
+    return sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else list(range(os.cpu_count()))
+
+
 def host_threads(limit):
-    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    return max(1, min(n, limit))
+    return max(1, min(len(host_cpus()), limit))
+
+
+def _ranges(cpus):
+    out, i = [], 0
+    while i < len(cpus):
+        j = i
+        while j + 1 < len(cpus) and cpus[j + 1] == cpus[j] + 1:
+            j += 1
+        out.append(f"{cpus[i]}-{cpus[j]}" if j > i else f"{cpus[i]}")
+        i = j + 1
+    return ",".join(out)
+
+
+def parallel(fn, items, threads):
+    """fn over items on `threads` Python threads (the oracle's C calls and
+    numpy's large operations release the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+    if threads <= 1:
+        return [fn(i) for i in items]
+    with ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(fn, items))
+
+
+def cpu_legs(single, multi, threads, unit, per_second, sample):
+    """The oracle timed twice on the host, each leg the median of 3 runs:
+    single() on one thread and multi() on `threads` threads, each returning
+    the amount of work it did (in the unit's own count). `per_second`
+    converts work / seconds into the reported value."""
+    legs = {}
+    for name, fn, n in (("single_thread", single, 1), ("all_cores", multi, threads)):
+        times, work = [], 0.0
+        for _ in range(3):
+            t0 = time.perf_counter()
+            work = fn()
+            times.append(time.perf_counter() - t0)
+        med = float(np.median(times))
+        legs[name] = {"value": round(per_second(work, med), 4), "threads": n, "median_s": round(med, 3),
+                      "runs_s": [round(t, 3) for t in times]}
+    return {"value": legs["all_cores"]["value"], "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": sample + f"; median of 3 runs per leg; host cores available {len(host_cpus())} "
+                               f"(affinity {_ranges(host_cpus())})",
+            "single_thread": legs["single_thread"], "all_cores": legs["all_cores"],
+            "affinity": _ranges(host_cpus())}
 
 
 def run_steps(args, step):
@@ -115,67 +162,92 @@ def expert_store(args, cfg, L, Ex, bb, dev, tag=None):
     return store
 
 
-def bench_decode(args, cfg, n_in, chain=False):
-    import torch
+class DecodeSchedule:
+    """Buffers of the staged decode workloads and the step the benchmark times.
 
-    from e0inputs import gen, gpu as G, workloads as W
-    from int4_gather_swiglu_amd import _lib as E
-    from int4_gather_swiglu_amd.pipeline import StagedPipeline
+    Step t: the side stream waits for the work already on main (the decode of
+    step t - 1), routes step t + 1 and runs the slot update (next = t + 1, in
+    use = t); the main stream decodes step t; main then waits for the side
+    stream. ``pre_decode(t)``, if given, is called right before the decode of
+    step t is enqueued on main (tests put a delay there to widen the window in
+    which the side stream rewrites slots)."""
 
-    dev = torch.device("cuda:0")
-    L, B, K, Ex, S, d, f = cfg.L, cfg.B, cfg.K, cfg.E, args.hot_slots or cfg.S, cfg.d, cfg.f
-    bb = gen.bundle_bytes(d, f)
-    # The full expert store filled on the GPU; per-step inputs drawn on the
-    # host and resident in HBM before the timed region.
-    store = expert_store(args, cfg, L, Ex, bb, dev)
-    pool = torch.zeros((L, S, bb), dtype=torch.uint8, device=dev)
-    xs = torch.from_numpy(np.stack([np.stack([W.activations(cfg, t, l) for l in range(L)])
-                                    for t in range(n_in)]).view(np.int16)).to(dev)
-    if cfg.router:
-        wr = torch.from_numpy(np.stack([W.router_weights(cfg, l) for l in range(L)]).view(np.int16)).to(dev)
-        lo = torch.empty((L, B, Ex), dtype=torch.float32, device=dev)
-    else:
-        logits = torch.from_numpy(np.stack([np.stack([W.given_logits(cfg, t, l) for l in range(L)])
-                                            for t in range(n_in)]).view(np.int16)).to(dev)
-    y = torch.empty((L, B, d), dtype=torch.float32, device=dev)
-    if chain:
-        r_ins = torch.from_numpy(np.stack([W.residual0(cfg, t) for t in range(n_in)])).to(dev)
-        norm_w = torch.from_numpy(np.stack([W.norm_weight(cfg, l) for l in range(L)]).view(np.int16)).to(dev)
-        r_out = torch.empty((L, d), dtype=torch.float32, device=dev)
-    dims = E.moe_dims(d, f, Ex, K)
-    pipe = StagedPipeline(dims, L, B, S, E.stack_from_bundles(store, d, f, bb, Ex * bb),
-                          E.stack_from_bundles(pool, d, f, bb, S * bb), device=dev, side_stream=not args.no_overlap,
-                          hot_set=bool(args.hot_slots))
-    rp = E.route_params(cfg.mode, K, cfg.n_groups, cfg.topk_groups, cfg.scale, cfg.eps)
+    def __init__(self, args, cfg, n_in, chain=False, pre_decode=None):
+        import torch
 
-    def route(buf, t, on_side):
+        from e0inputs import gen, workloads as W
+        from int4_gather_swiglu_amd import _lib as E
+        from int4_gather_swiglu_amd.pipeline import StagedPipeline
+
+        dev = torch.device("cuda:0")
+        L, B, K, Ex, S, d, f = cfg.L, cfg.B, cfg.K, cfg.E, args.hot_slots or cfg.S, cfg.d, cfg.f
+        self.cfg, self.n_in, self.chain, self.pre_decode = cfg, n_in, chain, pre_decode
+        self.L, self.B, self.K, self.Ex, self.S, self.d, self.f = L, B, K, Ex, S, d, f
+        self.bb = bb = gen.bundle_bytes(d, f)
+        # The full expert store filled on the GPU; per-step inputs drawn on the
+        # host and resident in HBM before the timed region.
+        self.store = store = expert_store(args, cfg, L, Ex, bb, dev)
+        self.pool = pool = torch.zeros((L, S, bb), dtype=torch.uint8, device=dev)
+        self.xs = torch.from_numpy(np.stack([np.stack([W.activations(cfg, t, l) for l in range(L)])
+                                             for t in range(n_in)]).view(np.int16)).to(dev)
         if cfg.router:
-            pipe.route_router(buf, rp, xs[t % n_in], wr, lo, on_side=on_side)
+            self.wr = torch.from_numpy(np.stack([W.router_weights(cfg, l) for l in range(L)]).view(np.int16)).to(dev)
+            self.lo = torch.empty((L, B, Ex), dtype=torch.float32, device=dev)
         else:
-            pipe.route_given(buf, rp, logits[t % n_in], on_side=on_side)
+            self.logits = torch.from_numpy(np.stack([np.stack([W.given_logits(cfg, t, l) for l in range(L)])
+                                                     for t in range(n_in)]).view(np.int16)).to(dev)
+        self.y = torch.empty((L, B, d), dtype=torch.float32, device=dev)
+        if chain:
+            self.r_ins = torch.from_numpy(np.stack([W.residual0(cfg, t) for t in range(n_in)])).to(dev)
+            self.norm_w = torch.from_numpy(np.stack([W.norm_weight(cfg, l) for l in range(L)]).view(np.int16)).to(dev)
+            self.r_out = torch.empty((L, d), dtype=torch.float32, device=dev)
+        dims = E.moe_dims(d, f, Ex, K)
+        self.pipe = StagedPipeline(dims, L, B, S, E.stack_from_bundles(store, d, f, bb, Ex * bb),
+                                   E.stack_from_bundles(pool, d, f, bb, S * bb), device=dev,
+                                   side_stream=not args.no_overlap, hot_set=bool(args.hot_slots))
+        self.rp = E.route_params(cfg.mode, K, cfg.n_groups, cfg.topk_groups, cfg.scale, cfg.eps)
+        self.ev_dec, self.ev_upd = events(args.steps), events(args.steps)
+        self.route(0, 0, False)
+        self.pipe.update(0, None)
+        self.pipe.join()
 
-    ev_dec, ev_upd = events(args.steps), events(args.steps)
-    route(0, 0, False)
-    pipe.update(0, None)
-    pipe.join()
+    def route(self, buf, t, on_side):
+        if self.cfg.router:
+            self.pipe.route_router(buf, self.rp, self.xs[t % self.n_in], self.wr, self.lo, on_side=on_side)
+        else:
+            self.pipe.route_given(buf, self.rp, self.logits[t % self.n_in], on_side=on_side)
 
-    def step(t, rec):
+    def step(self, t, rec):
+        pipe = self.pipe
         nb, cb = (t + 1) % 2, t % 2
         pipe.side_after_main()
         if rec is not None:
-            ev_upd[rec][0].record(pipe.side)
-        route(nb, t + 1, True)
+            self.ev_upd[rec][0].record(pipe.side)
+        self.route(nb, t + 1, True)
         pipe.update(nb, cb, after_main=False)
         if rec is not None:
-            ev_upd[rec][1].record(pipe.side)
-            ev_dec[rec][0].record(pipe.main)
-        if chain:
-            pipe.decode_chain(cb, r_ins[t % n_in], norm_w, CHAIN_EPS, y, r_out)
-        else:
-            pipe.decode(cb, xs[t % n_in], y)
+            self.ev_upd[rec][1].record(pipe.side)
+        if self.pre_decode is not None:
+            self.pre_decode(t)
         if rec is not None:
-            ev_dec[rec][1].record(pipe.main)
+            self.ev_dec[rec][0].record(pipe.main)
+        if self.chain:
+            pipe.decode_chain(cb, self.r_ins[t % self.n_in], self.norm_w, CHAIN_EPS, self.y, self.r_out)
+        else:
+            pipe.decode(cb, self.xs[t % self.n_in], self.y)
+        if rec is not None:
+            self.ev_dec[rec][1].record(pipe.main)
         pipe.join()
+
+
+def bench_decode(args, cfg, n_in, chain=False):
+    import torch
+
+    sch = DecodeSchedule(args, cfg, n_in, chain)
+    pipe, route, step = sch.pipe, sch.route, sch.step
+    L, B, Ex, S, d, f, bb = sch.L, sch.B, sch.Ex, sch.S, sch.d, sch.f, sch.bb
+    K = sch.K
+    ev_dec, ev_upd = sch.ev_dec, sch.ev_upd
 
     wall = run_steps(args, step)
     if int(pipe.err.item()):
@@ -229,15 +301,17 @@ CHAIN_EPS = 1e-6
 
 
 def cpu_chain(cfg, n_steps):
-    """Oracle chained decode (norm -> staged MoE -> residual per layer) on a
-    sample of steps; one thread (each layer needs the one before)."""
+    """Oracle chained decode (norm -> staged MoE -> residual per layer). One
+    token's layers run in sequence (each needs the one before); the all-core
+    leg runs independent tokens on separate threads."""
     import oracle
     from e0inputs import gen, workloads as W
 
-    steps = n_steps or 2
+    threads = host_threads(64)
     g = np.stack([W.norm_weight(cfg, l) for l in range(cfg.L)])
-    t_total = 0.0
-    for t in range(steps):
+    n_tok = max(threads, n_steps or 0)
+    toks = []
+    for t in range(n_tok):
         lg = np.stack([W.given_logits(cfg, t, l)[0] for l in range(cfg.L)]).astype(np.float32)
         idx, w = oracle.softmax_topk(lg, cfg.K)
         mats, so = [], np.full((cfg.L, cfg.E), -1, np.int32)
@@ -245,50 +319,104 @@ def cpu_chain(cfg, n_steps):
             for s_, e in enumerate(int(v) for v in idx[l]):
                 mats.append(gen.expert(cfg.seed, l, e, cfg.d, cfg.f))
                 so[l, e] = s_
-        t0 = time.perf_counter()
-        oracle.chain_decode(oracle.Experts(mats), cfg.K, so, cfg.E, cfg.d, cfg.f,
-                            W.residual0(cfg, t).astype(np.float64), g, CHAIN_EPS, idx, w)
-        t_total += time.perf_counter() - t0
-    return {"value": round(steps / t_total, 4), "unit": f"tok/s ({cfg.L}-layer chained stack, batch 1)",
-            "cores": 1, "kind": "oracle",
-            "sample": f"{steps} token(s) through {cfg.L} chained layers: the fp64 C oracle's chained decode, "
-                      f"1 thread; {t_total:.1f} s"}
+        toks.append((oracle.Experts(mats), so, W.residual0(cfg, t).astype(np.float64), idx, w))
+
+    def one(i):
+        P, so, r0, idx, w = toks[i]
+        oracle.chain_decode(P, cfg.K, so, cfg.E, cfg.d, cfg.f, r0, g, CHAIN_EPS, idx, w)
+        return 1
+
+    return cpu_legs(lambda: one(0), lambda: sum(parallel(one, range(n_tok), threads)), threads,
+                    f"tok/s ({cfg.L}-layer chained stack, batch 1)", lambda n, sec: n / sec,
+                    f"the fp64 C oracle's chained decode through {cfg.L} layers: 1 token on 1 thread; "
+                    f"{n_tok} independent tokens on {threads} threads")
 
 
 def cpu_decode(cfg, n_steps):
-    """Oracle staged decode (routing, slot rule, expert FFNs) on a sample of steps."""
+    """Oracle staged decode: routing and the slot rule outside the timing, then
+    the fp64 C oracle's staged FFNs over (layer, token) work. Single thread: a
+    fixed subset of layers (and, at batch > 1, of tokens); all cores: whole
+    steps split over layers. Reported as tokens through the whole stack per
+    second."""
     import oracle
     from e0inputs import gen, workloads as W
 
-    threads = host_threads(cfg.L)
-    steps = n_steps or (1 if cfg.B > 1 else max(1, min(8, threads // 2)))
-    t_total = 0.0
-    for t in range(steps):
-        pools, slot_of, xs, idxs, ws = [], [], [], [], []
+    threads = host_threads(64)
+    tb = cfg.B if cfg.B <= 4 else 4   # tokens per layer in the sample
+    n_steps = n_steps or (8 if cfg.B == 1 else 1)
+    rows = []                          # (pool mats [S], slot_of, x [tb][d], idx, w) per (step, layer)
+    for t in range(n_steps):
         for l in range(cfg.L):
             x = W.activations(cfg, t, l)
             lg = (oracle.router_logits(x, W.router_weights(cfg, l)) if cfg.router
                   else W.given_logits(cfg, t, l).astype(np.float32))
             idx, w = oracle.route(lg, cfg)
+            idx, w, x = idx[:tb], w[:tb], x[:tb]
             so = np.full(cfg.E, -1, np.int32)
             eo = np.full(cfg.S, -1, np.int32)
             oracle.slot_update(cfg.E, cfg.S, idx, [], so, eo)
             mats = {int(e): gen.expert(cfg.seed, l, int(e), cfg.d, cfg.f) for e in eo if e >= 0}
             first = next(iter(mats.values()))
-            pools += [mats.get(int(e), first) for e in eo]
-            slot_of.append(so)
-            xs.append(x)
-            idxs.append(idx)
-            ws.append(w)
-        P = oracle.Experts(pools)
-        t0 = time.perf_counter()
-        oracle.decode_layers(P, cfg.S, np.stack(slot_of), cfg.E, cfg.d, cfg.f, np.stack(xs), np.stack(idxs),
-                             np.stack(ws), n_threads=threads)
-        t_total += time.perf_counter() - t0
-    return {"value": round(steps * cfg.B / t_total, 4), "unit": f"tok/s ({cfg.L}-layer MoE stack, batch {cfg.B})",
-            "cores": threads, "kind": "oracle",
-            "sample": f"{steps} decode step(s) x {cfg.L} layers at batch {cfg.B}: staged FFNs of the fp64 C oracle, "
-                      f"{threads} threads over layers; {t_total:.1f} s"}
+            rows.append(([mats.get(int(e), first) for e in eo], so, x, idx, w))
+
+    def pack(sel):
+        P = oracle.Experts([m for i in sel for m in rows[i][0]])
+        return (P, np.stack([rows[i][1] for i in sel]), np.stack([rows[i][2] for i in sel]),
+                np.stack([rows[i][3] for i in sel]), np.stack([rows[i][4] for i in sel]))
+
+    n1 = 16 if cfg.B == 1 else 2
+    one_in, all_in = pack(range(n1)), pack(range(len(rows)))
+
+    def run(inp, n):
+        P, so, x, idx, w = inp
+        oracle.decode_layers(P, cfg.S, so, cfg.E, cfg.d, cfg.f, x, idx, w, n_threads=n)
+        return idx.shape[0] * idx.shape[1]   # (layer, token) units
+
+    return cpu_legs(lambda: run(one_in, 1), lambda: run(all_in, threads), threads,
+                    f"tok/s ({cfg.L}-layer MoE stack, batch {cfg.B})", lambda n, sec: n / cfg.L / sec,
+                    f"staged FFNs of the fp64 C oracle on the workload's routing and slot rule, {tb} token(s) per "
+                    f"layer: {n1} layer(s) on 1 thread; {n_steps} step(s) x {cfg.L} layers split over "
+                    f"{threads} threads; value = (layer, token) units per second / {cfg.L} layers")
+
+
+def cpu_prerouted(cfg, n_steps):
+    """Oracle prerouted step: every head's logits (fc1 over [hidden | K-hot |
+    K-hot], erf-GELU, fc2 + linear residual), softmax-top-K, then each staged
+    layer's routed experts plus the shared expert with unmerged LoRA. One
+    (head, layer) unit is independent of the others within a step."""
+    import oracle
+    from e0inputs import gen, workloads as W
+
+    threads = host_threads(64)
+    L, K = cfg.L, cfg.K
+    n_steps = n_steps or 4
+    P = W.prerouted_inputs(cfg, n_steps + 1)
+    heads = [W.head(cfg, j) for j in range(L)]
+    lor = [W.lora(cfg, l) for l in range(L)]
+    sh = [W.shared_expert(cfg, l) for l in range(L)]
+    R = np.concatenate([P.owner0[0][None], P.r0])
+    units = []
+    for t in range(n_steps):
+        for l in range(L):
+            ids = [int(e) for e in R[1 + l]]
+            mats = {e: gen.expert(cfg.seed, l, e, cfg.d, cfg.f) for e in ids}
+            units.append((t, l, oracle.Experts([mats.get(e, mats[ids[0]]) for e in range(cfg.E)]), R[1 + l].copy()))
+
+    def one(i):
+        t, l, ex, ids = units[i]
+        o = oracle.head_logits(heads[l], P.hin[t, l], R[l], None, K)
+        oracle.softmax_topk(o.astype(np.float32)[None], K)
+        x = P.hin[t, 1 + l]
+        oracle.moe_exact(ex, cfg.d, cfg.f, x[None], ids[None], np.full((1, K), 1.0 / K))
+        oracle.shared_lora(sh[l], lor[l], cfg.lora_r, cfg.lora_alpha_over_r, x, cfg.d, cfg.shared_f)
+        return 1
+
+    n1 = 16
+    return cpu_legs(lambda: sum(one(i) for i in range(n1)), lambda: sum(parallel(one, range(len(units)), threads)),
+                    threads, f"tok/s ({L} staged layers + heads, batch 1)", lambda n, sec: n / L / sec,
+                    f"the fp64 C oracle's head, routing, routed experts and shared expert with LoRA per staged "
+                    f"layer: {n1} layers on 1 thread; {n_steps} step(s) x {L} layers on {threads} threads; "
+                    f"value = layer units per second / {L} layers")
 
 
 # ---------------------------------------------------------------------------
@@ -348,21 +476,31 @@ def bench_prefill(args, cfg):
 
 
 def cpu_prefill(cfg, n_tok):
+    """Oracle sorted ordering (stable sort of the (token, k) pairs by expert,
+    each pair's FFN, combine in k order) on a sample of the prefill tokens:
+    one block of tokens on one thread; blocks of tokens on separate threads."""
     import oracle
     from e0inputs import gen, workloads as W
 
-    tok = np.arange(n_tok or 16)
-    x = W.activations(cfg, 0, 0)[tok]
-    idx, w = oracle.softmax_topk(W.given_logits(cfg, 0, 0)[tok].astype(np.float32), cfg.K)
-    ids = sorted(set(idx.ravel().tolist()))
+    threads = host_threads(64)
+    blk = n_tok or 32
+    x_all = W.activations(cfg, 0, 0)
+    idx_all, w_all = oracle.softmax_topk(W.given_logits(cfg, 0, 0).astype(np.float32), cfg.K)
+    n_blk = threads
+    tok = np.arange(blk * n_blk)
+    ids = sorted(set(idx_all[tok].ravel().tolist()))
     mats = {e: gen.expert(cfg.seed, 0, e, cfg.d, cfg.f) for e in ids}
-    lst = [mats.get(e, mats[ids[0]]) for e in range(cfg.E)]
-    t0 = time.perf_counter()
-    oracle.moe_sorted(oracle.Experts(lst), cfg.d, cfg.f, x, idx, w)
-    dt = time.perf_counter() - t0
-    return {"value": round(len(tok) / dt, 4), "unit": "tok/s (one MoE layer)", "cores": 1, "kind": "oracle",
-            "sample": f"{len(tok)} of the {cfg.B} prefill tokens through the sorted ordering of the fp64 C oracle, "
-                      f"single thread; {dt:.1f} s"}
+    ex = oracle.Experts([mats.get(e, mats[ids[0]]) for e in range(cfg.E)])
+
+    def one(b):
+        sl = slice(b * blk, (b + 1) * blk)
+        oracle.moe_sorted(ex, cfg.d, cfg.f, x_all[sl], idx_all[sl], w_all[sl])
+        return blk
+
+    return cpu_legs(lambda: one(0), lambda: sum(parallel(one, range(n_blk), threads)), threads,
+                    "tok/s (one MoE layer)", lambda n, sec: n / sec,
+                    f"the first prefill tokens through the sorted ordering of the fp64 C oracle: {blk} tokens on "
+                    f"1 thread; {n_blk} blocks of {blk} on {threads} threads")
 
 
 # ---------------------------------------------------------------------------
@@ -447,90 +585,123 @@ def bench_merge(args, cfg):
 
 
 def cpu_merge(cfg):
+    """The fp64 numpy merge oracle on the shared experts' matrices: the three
+    matrices of layer 0 on one thread; those of the first layers on all
+    threads."""
     from e0inputs import workloads as W
     from oracle import merge as M
 
-    sh, lo = W.shared_expert(cfg, 0), W.lora(cfg, 0)
-    t0 = time.perf_counter()
-    for m in range(3):
-        q, sc, bi = sh[m]
-        la, lb = lo[m]
-        M.merge_requant(q, sc, bi, lb.view(np.uint16), la.view(np.uint16), cfg.lora_alpha_over_r)
-    dt = time.perf_counter() - t0
-    return {"value": round(3 / dt, 3), "unit": "merged int4 g64 matrices/s", "cores": 1, "kind": "oracle",
-            "sample": f"the 3 shared-expert matrices of layer 0 through the oracle's fp32 numpy merge; {dt:.2f} s"}
+    threads = host_threads(64)
+    n_layers = max(2, min(cfg.L, threads))
+    mats = []
+    for l in range(n_layers):
+        sh, lo = W.shared_expert(cfg, l), W.lora(cfg, l)
+        for m in range(3):
+            q, sc, bi = sh[m]
+            la, lb = lo[m]
+            mats.append((q, sc, bi, lb.view(np.uint16), la.view(np.uint16)))
+
+    def one(i):
+        M.merge_requant(*mats[i], cfg.lora_alpha_over_r)
+        return 1
+
+    return cpu_legs(lambda: sum(one(i) for i in range(6)), lambda: sum(parallel(one, range(len(mats)), threads)),
+                    threads, "merged int4 g64 matrices/s", lambda n, sec: n / sec,
+                    f"the shared-expert matrices through the oracle's fp64 numpy merge: the 6 of layers 0-1 on "
+                    f"1 thread; the {len(mats)} of {n_layers} layers on {threads} threads")
 
 
 # ---------------------------------------------------------------------------
 # prerouted pipeline (35B tier, 32 staged layers)
 # ---------------------------------------------------------------------------
 
-def bench_prerouted(args, cfg, n_in):
-    import torch
+class PrerouterSchedule:
+    """Buffers of the prerouted pipeline and the step the benchmark times.
 
-    from e0inputs import gen, gpu as G, workloads as W
-    from int4_gather_swiglu_amd import _lib as E
-    from int4_gather_swiglu_amd.pipeline import PrerouterPipeline
+    Step t: the side stream runs the heads of step t (the routing of step
+    t + 1, one call for all heads) and then the slot update for step t + 1,
+    while the main stream decodes step t with the routing predicted one step
+    earlier: the one-token lead lets the prediction and the staging of step
+    t + 1 overlap step t's compute. The slot update waits for the decode of
+    step t - 1 (it may evict that step's experts); the decode of step t + 1
+    waits for the update (join). Routing state R[t % 3] is [L+1][1][K] (row
+    0: the unstaged owner of head 0). ``pre_decode(t)`` as in DecodeSchedule.
+    ``inputs`` (a workloads.Prerouted) replaces the drawn inputs if given."""
 
-    dev = torch.device("cuda:0")
-    L, K, Ex, S, d, f = cfg.L, cfg.K, cfg.E, args.hot_slots or cfg.S, cfg.d, cfg.f
-    bb = gen.bundle_bytes(d, f)
+    def __init__(self, args, cfg, n_in, pre_decode=None, inputs=None):
+        import torch
 
-    def f16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+        from e0inputs import gen, gpu as G, workloads as W
+        from int4_gather_swiglu_amd import _lib as E
+        from int4_gather_swiglu_amd.pipeline import PrerouterPipeline
 
-    store = expert_store(args, cfg, L, Ex, bb, dev)
-    pool = torch.zeros((L, S, bb), dtype=torch.uint8, device=dev)
-    heads = [W.head(cfg, j) for j in range(L)]
-    hd_t = [f16(np.stack([getattr(h, k) for h in heads])) for k in ("fc1_w", "fc1_b", "fc2_w", "fc2_b", "lin_w")]
-    bb_sh = gen.bundle_bytes(d, cfg.shared_f)
-    sh_store = torch.zeros((L, bb_sh), dtype=torch.uint8, device=dev)
-    for l in range(L):
-        G.fill_experts(sh_store[l].data_ptr(), bb_sh, cfg.seed, l, [0], d, cfg.shared_f, tag=gen.TAG_SHARED)
-    lor = [W.lora(cfg, l) for l in range(L)]
-    la = [f16(np.stack([lor[l][p][0] for l in range(L)])) for p in range(3)]
-    lb = [f16(np.stack([lor[l][p][1] for l in range(L)])) for p in range(3)]
-    P = W.prerouted_inputs(cfg, n_in)
-    hin = f16(P.hin[:, :, None, :])
-    owner0 = torch.from_numpy(P.owner0).to(dev)
-    dims = E.moe_dims(d, f, Ex, K)
-    shared = E.shared_from_tensors(sh_store, d, cfg.shared_f, la, lb, cfg.lora_alpha_over_r)
-    pipe = PrerouterPipeline(dims, L, 1, S, E.stack_from_bundles(store, d, f, bb, Ex * bb),
-                             E.stack_from_bundles(pool, d, f, bb, S * bb), E.heads_from_tensors(*hd_t),
-                             E.route_params(0, K), shared=shared, device=dev, side_stream=not args.no_overlap,
-                             hot_set=bool(args.hot_slots))
-    R = torch.zeros((3, L + 1, 1, K), dtype=torch.int32, device=dev)
-    Wt = torch.full((3, L + 1, 1, K), 1.0 / K, dtype=torch.float32, device=dev)
-    R[0, 0, 0] = owner0[0]
-    R[0, 1:, 0] = torch.from_numpy(P.r0).to(dev)
-    y = torch.empty((L, 1, d), dtype=torch.float32, device=dev)
-    ev_dec, ev_pre = events(args.steps), events(args.steps)
-    pipe.update_ids(R[0, 1:], None)
-    pipe.join()
+        dev = torch.device("cuda:0")
+        L, K, Ex, S, d, f = cfg.L, cfg.K, cfg.E, args.hot_slots or cfg.S, cfg.d, cfg.f
+        self.cfg, self.n_in, self.pre_decode = cfg, n_in, pre_decode
+        self.L, self.K, self.Ex, self.S, self.d, self.f = L, K, Ex, S, d, f
+        self.bb = bb = gen.bundle_bytes(d, f)
 
-    def step(t, rec):
-        # Step t: the side stream runs the heads of step t (routing of step t + 1,
-        # one call for all heads) and then the slot update for step t + 1, while
-        # the main stream decodes step t with the routing predicted one step
-        # earlier: the one-token lead lets the prediction and the staging of
-        # step t + 1 overlap step t's compute. The slot update waits for the
-        # decode of step t - 1 (it may evict that step's experts); the decode of
-        # step t + 1 waits for the update (join).
+        def f16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+        self.store = store = expert_store(args, cfg, L, Ex, bb, dev)
+        self.pool = pool = torch.zeros((L, S, bb), dtype=torch.uint8, device=dev)
+        heads = [W.head(cfg, j) for j in range(L)]
+        hd_t = [f16(np.stack([getattr(h, k) for h in heads])) for k in ("fc1_w", "fc1_b", "fc2_w", "fc2_b", "lin_w")]
+        self.bb_sh = bb_sh = gen.bundle_bytes(d, cfg.shared_f)
+        sh_store = torch.zeros((L, bb_sh), dtype=torch.uint8, device=dev)
+        for l in range(L):
+            G.fill_experts(sh_store[l].data_ptr(), bb_sh, cfg.seed, l, [0], d, cfg.shared_f, tag=gen.TAG_SHARED)
+        lor = [W.lora(cfg, l) for l in range(L)]
+        la = [f16(np.stack([lor[l][p][0] for l in range(L)])) for p in range(3)]
+        lb = [f16(np.stack([lor[l][p][1] for l in range(L)])) for p in range(3)]
+        self.P = P = inputs if inputs is not None else W.prerouted_inputs(cfg, n_in)
+        self.hin = f16(P.hin[:, :, None, :])
+        self.owner0 = torch.from_numpy(P.owner0).to(dev)
+        dims = E.moe_dims(d, f, Ex, K)
+        shared = E.shared_from_tensors(sh_store, d, cfg.shared_f, la, lb, cfg.lora_alpha_over_r)
+        self.pipe = pipe = PrerouterPipeline(dims, L, 1, S, E.stack_from_bundles(store, d, f, bb, Ex * bb),
+                                             E.stack_from_bundles(pool, d, f, bb, S * bb), E.heads_from_tensors(*hd_t),
+                                             E.route_params(0, K), shared=shared, device=dev,
+                                             side_stream=not args.no_overlap, hot_set=bool(args.hot_slots))
+        self.R = R = torch.zeros((3, L + 1, 1, K), dtype=torch.int32, device=dev)
+        self.Wt = torch.full((3, L + 1, 1, K), 1.0 / K, dtype=torch.float32, device=dev)
+        R[0, 0, 0] = self.owner0[0]
+        R[0, 1:, 0] = torch.from_numpy(P.r0).to(dev)
+        self.y = torch.empty((L, 1, d), dtype=torch.float32, device=dev)
+        self.ev_dec, self.ev_pre = events(args.steps), events(args.steps)
+        pipe.update_ids(R[0, 1:], None)
+        pipe.join()
+
+    def step(self, t, rec):
+        import torch
+        pipe, R, Wt, n_in = self.pipe, self.R, self.Wt, self.n_in
         c, n, p = t % 3, (t + 1) % 3, (t - 1) % 3
         with torch.cuda.stream(pipe.side):
-            R[n, 0, 0].copy_(owner0[(t + 1) % n_in])
+            R[n, 0, 0].copy_(self.owner0[(t + 1) % n_in])
         if rec is not None:
-            ev_pre[rec][0].record(pipe.side)
-        pipe.predict(hin[t % n_in], R[c], R[p] if t > 0 else None, R[n], Wt[n], on_side=True)
+            self.ev_pre[rec][0].record(pipe.side)
+        pipe.predict(self.hin[t % n_in], R[c], R[p] if t > 0 else None, R[n], Wt[n], on_side=True)
         if rec is not None:
-            ev_pre[rec][1].record(pipe.side)
+            self.ev_pre[rec][1].record(pipe.side)
         pipe.update_ids(R[n, 1:], R[c, 1:])
+        if self.pre_decode is not None:
+            self.pre_decode(t)
         if rec is not None:
-            ev_dec[rec][0].record(pipe.main)
-        pipe.decode_ids(R[c, 1:], Wt[c, 1:], hin[t % n_in, 1:], y)
+            self.ev_dec[rec][0].record(pipe.main)
+        pipe.decode_ids(R[c, 1:], Wt[c, 1:], self.hin[t % n_in, 1:], self.y)
         if rec is not None:
-            ev_dec[rec][1].record(pipe.main)
+            self.ev_dec[rec][1].record(pipe.main)
         pipe.join()
+
+
+def bench_prerouted(args, cfg, n_in):
+    from e0inputs import workloads as W
+
+    sch = PrerouterSchedule(args, cfg, n_in)
+    pipe, step = sch.pipe, sch.step
+    L, K, Ex, S, d, f, bb, bb_sh = sch.L, sch.K, sch.Ex, sch.S, sch.d, sch.f, sch.bb, sch.bb_sh
+    ev_dec, ev_pre = sch.ev_dec, sch.ev_pre
 
     wall = run_steps(args, step)
     if int(pipe.err.item()):
@@ -639,6 +810,7 @@ def main():
         cpu = (lambda: cpu_merge(W.PREROUTED35))
     else:
         res = bench_prerouted(args, W.PREROUTED35, 32)
+        cpu = (lambda: cpu_prerouted(W.PREROUTED35, args.cpu_steps))
     out = {"metric": METRIC, "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None,

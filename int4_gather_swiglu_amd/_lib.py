@@ -143,13 +143,16 @@ def bundle_bytes(d: int, f: int) -> int:
 
 
 def stack_from_bundles(base, d: int, f: int, slot_stride: int, layer_stride: int = 0) -> Stack:
-    """e0_stack over bundle-contiguous experts starting at tensor/pointer `base`."""
+    """e0_stack over bundle-contiguous experts starting at tensor/pointer `base`.
+    The returned struct holds a reference to a tensor `base`, so the memory its
+    pointers name lives as long as the struct."""
     addr = base if isinstance(base, int) else base.data_ptr()
     st = Stack()
     off = 0
     for i, sz in enumerate(bundle_part_sizes(d, f)):
         st.part[i] = Part(addr + off, slot_stride, layer_stride)
         off += sz
+    st._keep = None if isinstance(base, int) else base
     return st
 
 
@@ -231,17 +234,23 @@ def e0_slot_update_lru(dims: MoeDims, L: int, B: int, S: int, next_idx, cur_idx,
 def heads_from_tensors(fc1_w, fc1_b, fc2_w, fc2_b, lin_w) -> PrerouterHeads:
     """e0_prerouter_heads over stacked per-head fp16 tensors:
     fc1_w [H][hid][d+2E], fc1_b [H][hid] or None, fc2_w [H][E][hid],
-    fc2_b [H][E] or None, lin_w [H][E][d]."""
+    fc2_b [H][E] or None, lin_w [H][E][d]. The struct holds references to the
+    tensors, so the memory its pointers name lives as long as the struct."""
     def ps(t):
         return (t.data_ptr(), t[0].numel() * t.element_size()) if t is not None else (None, 0)
     (a, sa), (b, sb), (c, sc), (d_, sd), (e, se) = ps(fc1_w), ps(fc1_b), ps(fc2_w), ps(fc2_b), ps(lin_w)
-    return PrerouterHeads(a, sa, b, sb, c, sc, d_, sd, e, se, int(fc1_w.shape[1]), 0)
+    hd = PrerouterHeads(a, sa, b, sb, c, sc, d_, sd, e, se, int(fc1_w.shape[1]), 0)
+    hd._keep = (fc1_w, fc1_b, fc2_w, fc2_b, lin_w)
+    return hd
 
 
 def shared_from_tensors(store, d: int, f: int, lora_a=None, lora_b=None, lora_scale: float = 0.0) -> Shared:
     """e0_shared over per-layer bundles store [L][bundle] (one shared expert
-    per layer) and optional LoRA: lora_a[p] [L][r][in_p], lora_b[p] [L][out_p][r]."""
+    per layer) and optional LoRA: lora_a[p] [L][r][in_p], lora_b[p] [L][out_p][r].
+    The struct holds references to the tensors, so the memory its pointers name
+    lives as long as the struct."""
     sh = Shared()
+    sh._keep = (store, None if lora_a is None else list(lora_a), None if lora_b is None else list(lora_b))
     bb = bundle_bytes(d, f)
     sh.w = stack_from_bundles(store, d, f, bb, store[0].numel() * store.element_size())
     sh.d_ff = f

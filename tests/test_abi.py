@@ -175,3 +175,32 @@ def test_binding_has_no_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(E, "_LIB", None)
     with pytest.raises(RuntimeError, match="not built"):
         E.lib()
+
+
+def test_structs_keep_their_tensors_alive():
+    # The structs hold raw pointers; the helpers that build them from tensors
+    # keep those tensors referenced, so a caller that drops its own names (a
+    # set-up function returning only the struct) cannot free memory the
+    # library will later read.
+    import gc
+    import weakref
+
+    import torch
+    t = [torch.zeros((2, 8, 16), dtype=torch.int16) for _ in range(5)]
+    refs = [weakref.ref(x) for x in t]
+    hd = E.heads_from_tensors(*t)
+    st_t = torch.zeros((2, E.bundle_bytes(256, 128)), dtype=torch.uint8)
+    st_ref = weakref.ref(st_t)
+    st = E.stack_from_bundles(st_t, 256, 128, E.bundle_bytes(256, 128))
+    la = [torch.zeros((2, 4, 256), dtype=torch.int16) for _ in range(3)]
+    lb = [torch.zeros((2, 256, 4), dtype=torch.int16) for _ in range(3)]
+    lr = [weakref.ref(x) for x in la + lb]
+    sh_t = torch.zeros((2, E.bundle_bytes(256, 128)), dtype=torch.uint8)
+    sh_ref = weakref.ref(sh_t)
+    sh = E.shared_from_tensors(sh_t, 256, 128, la, lb, 2.0)
+    del t, st_t, la, lb, sh_t
+    gc.collect()
+    assert all(r() is not None for r in refs + lr) and st_ref() is not None and sh_ref() is not None
+    del hd, st, sh
+    gc.collect()
+    assert all(r() is None for r in refs + lr) and st_ref() is None and sh_ref() is None

@@ -3,8 +3,17 @@ heads over [hidden | current K-hot | previous K-hot] = 2560, fc1 -> erf-GELU
 -> fc2 plus the linear residual, prediction used as the routing, slot update
 of changed experts, staged decode with the shared expert and its unmerged
 rank-16 LoRA). Predicted routing and slot tables bit-exact; outputs rel-L2 <=
-1e-3. Planted hiddens are redrawn until every routing decision of the oracle's
-head logits has a margin >= 1e-3."""
+1e-3; the heads' logits element by element within LOGIT_ATOL of the oracle's
+fp64 logits. Planted hiddens are redrawn until every routing decision of the
+oracle's head logits has a margin >= 1e-3.
+
+LOGIT_ATOL: the kernel accumulates fp16 products in fp32 over 2560 (fc1),
+512 (fc2) and 2048 (linear residual) inputs whose absolute sums stay below
+about 40 here; a few dozen roundings of 2^-24 relative to that is under 1e-5,
+and erf in fp32 adds less. 1e-4 leaves a margin and is about a thousandth of
+what the fc1 -> GELU -> fc2 branch contributes to a logit (about 0.2), so an
+error in that branch, which the planted +8 .. +6.5 targets hide from the
+routing ids, still fails."""
 import numpy as np
 import pytest
 
@@ -15,6 +24,7 @@ from tests import gpu_util as U
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
 DELTA = 1e-3
+LOGIT_ATOL = 1e-4
 
 
 def E():
@@ -59,12 +69,16 @@ def test_prerouted35b_pipeline_steps():
         if t < steps:
             R[t][0] = owner0[t]
 
+    O = {}
+
     def accept(t, j, h):
         cur = R[t][j]
         prev = R[t - 1][j] if t > 0 else None
-        o = oracle.head_logits(heads[j], h, cur, prev, K).astype(np.float32)[None]
+        o64 = oracle.head_logits(heads[j], h, cur, prev, K)
+        o = o64.astype(np.float32)[None]
         if oracle.route_margin(o, cfg) < DELTA:
             return False
+        O[(t, j)] = o64
         idx, w = oracle.softmax_topk(o, K)
         R[t + 1][j + 1] = idx[0]
         Wt[t + 1][j + 1] = w[0]
@@ -91,11 +105,12 @@ def test_prerouted35b_pipeline_steps():
         Rd[t, 0, 0] = U.i32(owner0[t])
     hin = U.f16(P.hin[:, :, None, :])  # [steps][L+1][1][d]
     ys = U.empty((steps, L, 1, cfg.d))
+    lo = U.empty((steps, L, 1, cfg.E))
     recs = []
     pipe.update_ids(Rd[0, 1:], None)
     pipe.join()
     for t in range(steps):
-        pipe.predict(hin[t], Rd[t], Rd[t - 1] if t > 0 else None, Rd[t + 1], Wd[t + 1])
+        pipe.predict(hin[t], Rd[t], Rd[t - 1] if t > 0 else None, Rd[t + 1], Wd[t + 1], logits_out=lo[t])
         Tt.cuda.current_stream().synchronize()
         pipe.side.synchronize()
         recs.append(dict(slot_of=pipe.slot_of.cpu().numpy(), expert_of=pipe.expert_of.cpu().numpy()))
@@ -112,6 +127,11 @@ def test_prerouted35b_pipeline_steps():
         assert np.abs(Wh[t, 1:] - Wt[t][1:]).max() < 1e-5
     rep = np.mean([len(set(Rh[t, 1 + l]) & set(Rh[t - 1, 1 + l])) / K for t in range(2, steps + 1) for l in range(L)])
     print("realized repeat rate", rep)
+    # 1b. every head's logits, element by element
+    lh = lo.cpu().numpy()[:, :, 0]
+    dl = max(float(np.abs(lh[t, j] - O[(t, j)]).max()) for t in range(steps) for j in range(L))
+    print("head logits: largest |gpu - oracle|", dl)
+    assert dl <= LOGIT_ATOL
     # 2. slot tables bit-exact against the oracle's rule
     so = np.full((L, cfg.E), -1, np.int32)
     eo = np.full((L, cfg.S), -1, np.int32)
@@ -131,6 +151,6 @@ def test_prerouted35b_pipeline_steps():
         routed, _ = oracle.moe_exact(oracle.Experts(lst), cfg.d, cfg.f, x, ids[None], Wh[t, 1 + l][None].astype(np.float64))
         sh = oracle.shared_lora(W.shared_expert(cfg, l), lor[l], cfg.lora_r, cfg.lora_alpha_over_r, x[0], cfg.d, cfg.shared_f)
         ref = routed[0] + sh
-        rs.append(U.rel_l2(y[t, l, 0], ref))
+        rs.append(U.assert_close(y[t, l, 0], ref, TOL, 1e-4, (t, l))[0])
     print("prerouted rel-L2", rs)
     assert max(rs) <= TOL
