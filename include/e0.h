@@ -227,6 +227,26 @@ e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, int32_t B, co
                                int32_t *dev_err, void *stream);
 
 /*
+ * e0_moe_staged_decode_noalloc — e0_moe_staged_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, kernels and results as
+ * e0_moe_staged_decode, without ws / ws_bytes: the workspace is a fixed device
+ * array of E0_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU,
+ * held until the process ends. The call allocates nothing.
+ *  Sizes whose workspace (e0_workspace_bytes(E0_OP_STAGED_DECODE, ...)) is
+ *  larger than the array return E0_ERR_CAPACITY before anything is enqueued.
+ *  The first call on a device looks up the array's address on that device
+ *  (hipGetSymbolAddress; a failure returns E0_ERR_HIP); later calls reuse it.
+ *  All calls on one GPU share the array: calls that may run at the same time
+ *  on one GPU (other streams, other host threads) race and must not overlap.
+ */
+#define E0_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+e0_status e0_moe_staged_decode_noalloc(const e0_moe_dims *dims, int32_t L, int32_t B, const uint16_t *x,
+                                       const int32_t *idx, const float *w, const int32_t *slot_of, int32_t S,
+                                       const e0_stack *pool, const e0_shared *shared, float *y, int32_t *dev_err,
+                                       void *stream);
+
+/*
  * e0_moe_sorted_prefill — the whole-layer path (jaehun.me report 3.1;
  * discuss.pytorch.kr paths table: a layer's experts all resident, then a
  * sorted gather): the T*K (token, k) pairs are grouped by expert (the order

@@ -18,9 +18,10 @@ E0_DEV_BAD_ID, E0_DEV_NOT_RESIDENT, E0_DEV_NO_SLOT = 1, 2, 4
 (E0_OP_ROUTE, E0_OP_PREROUTER, E0_OP_STAGED_DECODE, E0_OP_SORTED_PREFILL, E0_OP_SLOT_UPDATE,
  E0_OP_CHAINED_DECODE) = range(6)
 
+E0_NOALLOC_SCRATCH_BYTES = 32 << 20  # size of the fixed workspace of e0_moe_staged_decode_noalloc
 EXPORTS = ["e0_abi_version", "e0_status_string", "e0_workspace_bytes", "e0_route", "e0_prerouter",
            "e0_moe_staged_decode", "e0_moe_sorted_prefill", "e0_slot_update", "e0_moe_chained_decode",
-           "e0_lora_merge_requant", "e0_slot_update_lru"]
+           "e0_lora_merge_requant", "e0_slot_update_lru", "e0_moe_staged_decode_noalloc"]
 
 
 class E0Error(RuntimeError):
@@ -94,8 +95,11 @@ def lib() -> C.CDLL:
         L.e0_moe_chained_decode.argtypes = [C.POINTER(MoeDims), i32, vp, vp, C.c_float, vp, vp, vp, i32,
                                             C.POINTER(Stack), vp, vp, vp, sz, vp, vp]
         L.e0_lora_merge_requant.argtypes = [i32, i32, vp, vp, vp, vp, vp, i32, C.c_float, vp, vp, vp, vp]
+        L.e0_moe_staged_decode_noalloc.argtypes = [C.POINTER(MoeDims), i32, i32, vp, vp, vp, vp, i32,
+                                                   C.POINTER(Stack), C.POINTER(Shared), vp, vp, vp]
         for n in ("e0_route", "e0_prerouter", "e0_moe_staged_decode", "e0_moe_sorted_prefill", "e0_slot_update",
-                  "e0_moe_chained_decode", "e0_lora_merge_requant", "e0_slot_update_lru"):
+                  "e0_moe_chained_decode", "e0_lora_merge_requant", "e0_slot_update_lru",
+                  "e0_moe_staged_decode_noalloc"):
             getattr(L, n).restype = C.c_int32
         _LIB = L
     return _LIB
@@ -192,6 +196,15 @@ def e0_moe_staged_decode(dims: MoeDims, L: int, B: int, x, idx, w, slot_of, S: i
                                       C.byref(pool), C.byref(shared) if shared is not None else None, _ptr(y),
                                       _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
                                       _ptr(dev_err), _stream(stream)), "e0_moe_staged_decode")
+
+
+def e0_moe_staged_decode_noalloc(dims: MoeDims, L: int, B: int, x, idx, w, slot_of, S: int, pool: Stack,
+                                 shared: Shared | None, y, dev_err, stream=None):
+    """The staged decode with the library's own fixed workspace (allocates nothing)."""
+    _check(lib().e0_moe_staged_decode_noalloc(C.byref(dims), L, B, _ptr(x), _ptr(idx), _ptr(w), _ptr(slot_of), S,
+                                              C.byref(pool), C.byref(shared) if shared is not None else None,
+                                              _ptr(y), _ptr(dev_err), _stream(stream)),
+           "e0_moe_staged_decode_noalloc")
 
 
 def e0_moe_chained_decode(dims: MoeDims, L: int, r_in, norm_w, eps: float, idx, w, slot_of, S: int, pool: Stack,

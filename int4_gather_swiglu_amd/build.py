@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libe0.so")
-SOURCES = ["api.hip", "route.hip", "decode.hip", "slot.hip", "prerouter.hip", "prefill.hip", "merge.hip"]
+SOURCES = ["api.hip", "route.hip", "decode.hip", "slot.hip", "prerouter.hip", "prefill.hip", "merge.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -204,3 +204,18 @@ def test_structs_keep_their_tensors_alive():
     del hd, st, sh
     gc.collect()
     assert all(r() is None for r in refs + lr) and st_ref() is None and sh_ref() is None
+
+
+def test_noalloc_decode_refuses_sizes_beyond_its_array():
+    # A decode whose workspace exceeds the fixed array is refused on the host,
+    # before the device is touched (pointers are never dereferenced).
+    L = E.lib()
+    dims = E.moe_dims(2048, 2048, 1024, 8)
+    need = E.workspace_bytes(E.E0_OP_STAGED_DECODE, dims, 64, 64, 0)
+    assert need > E.E0_NOALLOC_SCRATCH_BYTES
+    st = E.stack_from_bundles(FAKE, 2048, 2048, 1 << 20)
+    rc = L.e0_moe_staged_decode_noalloc(C.byref(dims), 64, 64, FAKE, FAKE, FAKE, FAKE, 128, C.byref(st), None,
+                                        FAKE, FAKE, None)
+    assert rc == E.E0_ERR_CAPACITY
+    assert L.e0_moe_staged_decode_noalloc(None, 1, 1, FAKE, FAKE, FAKE, FAKE, 8, C.byref(st), None, FAKE, FAKE,
+                                          None) == E.E0_ERR_INVALID_ARG
