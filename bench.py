@@ -45,6 +45,7 @@ def parse():
                     choices=["decode35b", "prefill35b", "decode8b_b1", "decode8b_b32", "prerouted35b", "chain35b",
                              "merge35b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak probes")
     ap.add_argument("--no-overlap", action="store_true", help="run the slot update on the decode stream")
     ap.add_argument("--host-store", action="store_true",
                     help="keep the expert store in pinned host memory (the HBM slot pool as its cache; the slot "
@@ -762,6 +763,38 @@ def recorded_traffic(workload):
     return int(d["hbm_bytes_per_launch"])
 
 
+def measure_peaks():
+    """What this GPU sustains at its actual clock: a plain streaming read of a
+    2 GiB device buffer (larger than every on-chip cache) and independent fp16
+    MFMAs on 1024 workgroups (four wavefronts per SIMD), each the median of 5
+    launches timed with events."""
+    import torch
+
+    from int4_gather_swiglu_amd import _lib as E
+    buf = torch.ones(2 << 30, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    E.e0_probe_stream_read(buf, sink)
+    ev = events(5)
+    for a, b in ev:
+        a.record()
+        E.e0_probe_stream_read(buf, sink)
+        b.record()
+    torch.cuda.synchronize()
+    read_gbs = buf.numel() / (float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3) / 1e9
+    del buf
+    flop = E.e0_probe_mfma(1024, 1000, sink)
+    ev = events(5)
+    for a, b in ev:
+        a.record()
+        E.e0_probe_mfma(1024, 1000, sink)
+        b.record()
+    torch.cuda.synchronize()
+    mfma_tfs = flop / (float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3) / 1e12
+    return {"hbm_read_GBps": round(read_gbs, 1), "mfma_f16_TFLOPs": round(mfma_tfs, 1),
+            "probes": "e0_probe_stream_read over 2 GiB (16-byte streaming loads); e0_probe_mfma, 1024 workgroups "
+                      "x 4 waves x 1000 rounds of 8 independent v_mfma_f32_32x32x16_f16; median of 5 each"}
+
+
 def calibrate_copy(mib):
     import torch
     n = mib << 20
@@ -830,6 +863,13 @@ def main():
             out["config"]["workload"] += ", expert store in pinned host memory (HBM slots as its cache)"
     if "roofline" in out:
         out["roofline"]["traffic"] = recorded_traffic(wl)
+        if not args.no_peaks:
+            pk = measure_peaks()
+            rf = out["roofline"]
+            mp = pk["mfma_f16_TFLOPs"] if rf["unit"] == "TFLOP/s" else pk["hbm_read_GBps"]
+            rf["measured_peak"] = mp
+            rf["frac_measured"] = round(rf["achieved"] / mp, 4)
+            out["measured_peaks"] = pk
     if not args.no_cpu_baseline and cpu is not None:
         out["cpu_baseline"] = cpu()
     print(json.dumps(out), flush=True)

@@ -382,6 +382,9 @@ e0_status e0_moe_chained_decode(const e0_moe_dims *dims, int32_t L, const float 
  * then per (row, group), with lo/hi the group's least/largest w':
  *   s' = fp16((hi - lo) / 15),  b' = fp16(lo),
  *   q' = s' == 0 ? 0 : min(15, max(0, round_half_even((w' - b') / s'))).
+ * The definition is exact arithmetic; computed in fp32 as above, a code (or
+ * an fp16 scale or bias) can differ from the exact one by one step only where
+ * the exact value lies within the fp32 rounding error of a rounding flip.
  *  rows, cols: rows % 8 == 0, cols % 64 == 0, rows * cols < 2^31; r in 1 .. 64.
  *  q, q_out: device uint32 [rows][cols/8] (code c at bits 4*(c%8) of word
  *  c/8); s, b, s_out, b_out: device fp16 bit patterns in the stacks' 8-row
@@ -394,6 +397,20 @@ e0_status e0_moe_chained_decode(const e0_moe_dims *dims, int32_t L, const float 
 e0_status e0_lora_merge_requant(int32_t rows, int32_t cols, const uint32_t *q, const uint16_t *s, const uint16_t *b,
                                 const uint16_t *lora_b, const uint16_t *lora_a, int32_t r, float alpha_over_r,
                                 uint32_t *q_out, uint16_t *s_out, uint16_t *b_out, void *stream);
+
+/*
+ * Measurement probes (not part of the method): what this GPU sustains, for
+ * roofline fractions against measured as well as published peaks.
+ *  e0_probe_stream_read: reads `bytes` (multiple of 16, src 16-byte aligned)
+ *    of device memory once with 16-byte streaming loads on 4096 workgroups;
+ *    sink: device uint32 (practically never written).
+ *  e0_probe_mfma: `blocks` workgroups of four wavefronts, each running `iters`
+ *    rounds of eight independent v_mfma_f32_32x32x16_f16; *flop (host, may be
+ *    NULL) receives the dense FLOP count of the launch.
+ * Both only enqueue on `stream`; E0_ERR_INVALID_ARG on bad arguments.
+ */
+e0_status e0_probe_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+e0_status e0_probe_mfma(int32_t blocks, int32_t iters, uint32_t *sink, double *flop, void *stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,8 @@ E0_DEV_BAD_ID, E0_DEV_NOT_RESIDENT, E0_DEV_NO_SLOT = 1, 2, 4
 E0_NOALLOC_SCRATCH_BYTES = 32 << 20  # size of the fixed workspace of e0_moe_staged_decode_noalloc
 EXPORTS = ["e0_abi_version", "e0_status_string", "e0_workspace_bytes", "e0_route", "e0_prerouter",
            "e0_moe_staged_decode", "e0_moe_sorted_prefill", "e0_slot_update", "e0_moe_chained_decode",
-           "e0_lora_merge_requant", "e0_slot_update_lru", "e0_moe_staged_decode_noalloc"]
+           "e0_lora_merge_requant", "e0_slot_update_lru", "e0_moe_staged_decode_noalloc",
+           "e0_probe_stream_read", "e0_probe_mfma"]
 
 
 class E0Error(RuntimeError):
@@ -97,9 +98,11 @@ def lib() -> C.CDLL:
         L.e0_lora_merge_requant.argtypes = [i32, i32, vp, vp, vp, vp, vp, i32, C.c_float, vp, vp, vp, vp]
         L.e0_moe_staged_decode_noalloc.argtypes = [C.POINTER(MoeDims), i32, i32, vp, vp, vp, vp, i32,
                                                    C.POINTER(Stack), C.POINTER(Shared), vp, vp, vp]
+        L.e0_probe_stream_read.argtypes = [vp, sz, vp, vp]
+        L.e0_probe_mfma.argtypes = [i32, i32, vp, C.POINTER(C.c_double), vp]
         for n in ("e0_route", "e0_prerouter", "e0_moe_staged_decode", "e0_moe_sorted_prefill", "e0_slot_update",
                   "e0_moe_chained_decode", "e0_lora_merge_requant", "e0_slot_update_lru",
-                  "e0_moe_staged_decode_noalloc"):
+                  "e0_moe_staged_decode_noalloc", "e0_probe_stream_read", "e0_probe_mfma"):
             getattr(L, n).restype = C.c_int32
         _LIB = L
     return _LIB
@@ -276,3 +279,16 @@ def shared_from_tensors(store, d: int, f: int, lora_a=None, lora_b=None, lora_sc
             sh.lora_b[p] = lora_b[p].data_ptr()
             sh.lora_b_layer_stride[p] = lora_b[p][0].numel() * lora_b[p].element_size()
     return sh
+
+
+def e0_probe_stream_read(src, sink, stream=None):
+    """One streaming read of the whole device tensor `src` (measurement probe)."""
+    _check(lib().e0_probe_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)),
+           "e0_probe_stream_read")
+
+
+def e0_probe_mfma(blocks: int, iters: int, sink, stream=None) -> float:
+    """Independent fp16 MFMAs on `blocks` workgroups (measurement probe); returns the launch's FLOP."""
+    flop = C.c_double(0.0)
+    _check(lib().e0_probe_mfma(blocks, iters, _ptr(sink), C.byref(flop), _stream(stream)), "e0_probe_mfma")
+    return flop.value
