@@ -220,18 +220,6 @@ E0_DEV uint32_t and_or_v(uint32_t x, uint32_t m, uint32_t c) {
     return r;
 }
 
-// Weights 2p and 2p + 1 of one code word: s * q + b with one rounding each.
-// Byte p holds (q_2p, q_2p+1); placing it in both halves and masking gives
-// (1024 + q_2p, 1024 + 16 q_2p+1) by bit placement, and one fma with
-// (1, 1/16) and (-1024, -64) turns that into (q_2p, q_2p+1) exactly.
-E0_DEV f16x2 dequant_pair(uint32_t w, int p, f16x2 s2, f16x2 b2, uint32_t m, uint32_t c) {
-    const f16x2 kmul = f16x2{(f16)1.0f, (f16)0.0625f};
-    const f16x2 kadd = f16x2{(f16)-1024.0f, (f16)-64.0f};
-    const uint32_t dup = __builtin_amdgcn_perm(w, w, 0x0c000c00u | (uint32_t)p << 16 | (uint32_t)p);
-    const f16x2 q = __builtin_elementwise_fma(as_h2(and_or_v(dup, m, c)), kmul, kadd);
-    return __builtin_elementwise_fma(q, s2, b2);
-}
-
 // One 128-row M-tile (rows m0 .. of expert e) times 32 * NB * 4 output
 // columns, of which the first NMB 32-row blocks are computed. GATEUP: the two
 // B operands of a wave are the gate and the up column of one d_ff index, and
@@ -284,7 +272,9 @@ E0_DEV void prefill_tile(const PrefillArgs &a, uint16_t (*s_a)[kTM * kARow], int
             const int c = lslot ^ (r & 15);
             const uint16_t *src = abase + arow[i] * alen + st * kStepK + c * 8;
             const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(buf * kTM * kARow + (wv * 32 + 4 * i) * kStepK) * 2);
-            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "memory", "m0");
+            // m0 holds the wave's LDS destination (lane L lands at m0 + 16 L);
+            // the {m0} operand makes the compiler set it and know it is used.
+            asm volatile("global_load_lds_dwordx4 %1, off" ::"{m0}"(dst), "v"(src) : "memory");
         }
     };
 
