@@ -85,7 +85,8 @@ struct DecodeArgs {
     uint64_t epoch;
     int units;        // K + (shared expert ? 1 : 0)
     int nch;          // h half blocks (flags) per unit: d_ff / 16
-    int n_lora;       // lora items (L with LoRA, else 0)
+    int n_lora;       // lora items (L * lora_parts with LoRA, else 0)
+    int lora_parts;   // lora items per layer: 8 of the 2r dot products each
     int n_gu;         // gate/up items per layer (units * d_ff / 64)
     int n_dn;         // down items per layer
     int lag;          // the down items of layer l follow the gate/up items of layer l + lag
@@ -1170,7 +1171,12 @@ constexpr int kBlkSum = 32;
 constexpr int kChainSplit = 2;  // wavefronts per h half block in chained gate/up items
 constexpr int kChainD = 2048;   // d_model of chained calls (one 32-input slice per lane)
 
-E0_DEV uint64_t *gu_flags(const DecodeArgs &a, int l) { return a.flags + a.L + (int64_t)l * a.units * a.nch; }
+constexpr int kLoraJobs = 2 * kFuseWaves;          // dot products per lora item (two per wavefront)
+constexpr int kMaxLoraParts = 2 * kMaxR / kLoraJobs;  // lora items (and flags) per layer at most
+
+E0_DEV uint64_t *gu_flags(const DecodeArgs &a, int l) {
+    return a.flags + (int64_t)a.L * kMaxLoraParts + (int64_t)l * a.units * a.nch;
+}
 
 // h block of (layer l, unit u, 32-column group g): the down input h[32g ..
 // 32g + 32) in the form the down dot product takes (see dot_word_m2).
@@ -1178,23 +1184,68 @@ E0_DEV uint32_t *hblk(const DecodeArgs &a, int l, int u, int g) {
     return a.hblk + (((int64_t)l * a.units + u) * (a.f / 32) + g) * kBlk;
 }
 
-E0_DEV void fused_lora_item(const DecodeArgs &a, int l) {
+// Partial sums of the shared expert's LoRA A_down h of layer l: [nch][r], entry
+// (hb, i) = sum over the 16 hidden units of half block hb of A_down[i][unit] h[unit],
+// published by that half block's gate/up wavefront (in the layer's h rows of the
+// workspace, which this path does not otherwise use: nch * r <= (K + 1) * d_ff).
+E0_DEV float *lpart(const DecodeArgs &a, int l) { return hrow(a, l, 0); }
+
+// sum over i < r of b[i] * v[i], b fp16 and v fp32, both in LDS; 16-byte steps
+// when r is a multiple of 8 (b and v 16-byte aligned), else one at a time.
+E0_DEV float lds_dot_r(const uint16_t *b, const float *v, int r) {
+    float acc = 0.0f;
+    if ((r & 7) == 0) {
+        for (int i = 0; i < r; i += 8) {
+            const u32x4 bv = *reinterpret_cast<const u32x4 *>(b + i);
+            const f32x4 v0 = *reinterpret_cast<const f32x4 *>(v + i);
+            const f32x4 v1 = *reinterpret_cast<const f32x4 *>(v + i + 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f16x2 b2 = as_h2(bv[q]);
+                const float x0 = q < 2 ? v0[2 * q] : v1[2 * q - 4];
+                const float x1 = q < 2 ? v0[2 * q + 1] : v1[2 * q - 3];
+                acc += (float)b2[0] * x0 + (float)b2[1] * x1;
+            }
+        }
+    } else {
+        for (int i = 0; i < r; ++i) acc += h2f(b[i]) * v[i];
+    }
+    return acc;
+}
+
+// Lora item `part` of layer l: dot products part * kLoraJobs + {w, w + 4} of
+// the layer's 2r (A_gate x, then A_up x), wavefront w; every load of both is
+// issued before either is summed. The single-launch path runs at d_model 2048.
+E0_DEV void fused_lora_item(const DecodeArgs &a, int l, int part) {
+    constexpr int kC = 2048 / 512;  // 16-byte chunks per lane of a 2048-long row
     const int lane = threadIdx.x & 63, wv = wave_id();
     const uint16_t *xt = a.x + (int64_t)l * a.d;
-    for (int job = wv; job < 2 * a.r; job += kFuseWaves) {
-        const int p = job / a.r, i = job % a.r;
-        const uint16_t *arow = a.la[p] + (int64_t)l * (a.la_ls[p] / 2) + (int64_t)i * a.d;
-        float acc = 0.0f;
-        for (int c = lane * 8; c < a.d; c += 512) {
-            const u32x4 av = *reinterpret_cast<const u32x4 *>(arow + c);
-            const u32x4 xv = *reinterpret_cast<const u32x4 *>(xt + c);
+    u32x4 xv[kC], av[2][kC];
+    bool on[2];
+    int p[2], i[2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_fdot2(as_h2(av[j]), as_h2(xv[j]), acc, false);
-        }
-        acc = wave_sum(acc);
-        if (lane == 0) coherent_store(a.lora_a + ((int64_t)l * 3 + p) * a.r + i, acc);
+    for (int c = 0; c < kC; ++c) xv[c] = *reinterpret_cast<const u32x4 *>(xt + c * 512 + lane * 8);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int job = part * kLoraJobs + wv + q * kFuseWaves;
+        on[q] = job < 2 * a.r;
+        p[q] = on[q] ? job / a.r : 0;
+        i[q] = on[q] ? job % a.r : 0;
+        const uint16_t *arow = a.la[p[q]] + (int64_t)l * (a.la_ls[p[q]] / 2) + (int64_t)i[q] * a.d;
+#pragma unroll
+        for (int c = 0; c < kC; ++c) av[q][c] = *reinterpret_cast<const u32x4 *>(arow + c * 512 + lane * 8);
     }
-    signal_ready(a.flags + l, a.epoch);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kC; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_fdot2(as_h2(av[q][c][j]), as_h2(xv[c][j]), acc, false);
+        acc = wave_sum(acc);
+        if (on[q] && lane == 0) coherent_store(a.lora_a + ((int64_t)l * 3 + p[q]) * a.r + i[q], acc);
+    }
+    signal_ready(a.flags + (int64_t)l * kMaxLoraParts + part, a.epoch);
 }
 
 // Chained decode: the fp16 input slice of this lane (inputs 32 lane .. +31)
@@ -1273,7 +1324,8 @@ E0_DEV int routed_slot(const DecodeArgs &a, int l, int k, int &bits) {
 // block 2cg + j (both batches requested before the wait), meet in LDS, and
 // the first publishes the half block.
 template <int NP, bool SHARED, bool CHAIN = false>
-E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *s_small, float *s_r = nullptr) {
+E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *s_small, float *s_r = nullptr,
+                              uint16_t *s_lb = nullptr) {
     // Chained items: kChainSplit wavefronts share a half block (the wait for
     // the previous layer puts every batch on the critical path, so each
     // wavefront computes fewer of them).
@@ -1306,12 +1358,11 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *
     const int slot = SHARED ? 0 : routed_slot(a, l, u, bits);
     if (bits && cg == 0 && threadIdx.x == 0) set_err(a.err, bits);
     const bool lora = SHARED && a.r > 0;
-    if (lora) {
-        // A x of this layer, from its lora item (the whole workgroup waits).
-        if (!wait_ready(a.flags + l, 1, a.epoch) && threadIdx.x == 0) set_err(a.err, E0_DEV_SYNC_TIMEOUT);
-        if (threadIdx.x < 2 * a.r) s_av[threadIdx.x] = coherent_load(a.lora_a + (int64_t)l * 3 * a.r + threadIdx.x);
-        __syncthreads();
-    }
+    // LoRA rows of this wavefront's 16 hidden units (shared expert): B_gate and
+    // B_up rows in LDS, and A_down's 16 columns of them in registers (lane i < r
+    // holds row i) for the partial A_down h this half block publishes.
+    uint16_t *s_lbw = s_lb ? s_lb + wv * 2 * kHalfBlk * kMaxR : nullptr;
+    u32x4 adn[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
     if (slot >= 0) {
         rsrc_t qr[2], sr[2], br[2];
 #pragma unroll
@@ -1349,6 +1400,32 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *
         Stage A, B;
         load(0, A);
         load(1, B);
+        if (lora) {
+            // After the first weight loads: the LoRA rows, then the wait for
+            // this layer's A x (its lora item) by the whole workgroup.
+            constexpr int kLbMax = 2 * kHalfBlk * kMaxR / kWave;
+            const int nlb = 2 * kHalfBlk * a.r;
+            uint16_t lbv[kLbMax];
+#pragma unroll
+            for (int j = 0; j < kLbMax; ++j) {
+                const int i = lane + j * kWave;
+                const int m = i / (kHalfBlk * a.r), rem = i % (kHalfBlk * a.r);
+                lbv[j] = i < nlb ? a.lb[m][(int64_t)l * (a.lb_ls[m] / 2) + (int64_t)row0 * a.r + rem] : (uint16_t)0;
+            }
+            if (lane < a.r) {
+                const u32x4 *ap = reinterpret_cast<const u32x4 *>(a.la[2] + (int64_t)l * (a.la_ls[2] / 2) +
+                                                                  (int64_t)lane * a.f + row0);
+                adn[0] = ap[0];
+                adn[1] = ap[1];
+            }
+#pragma unroll
+            for (int j = 0; j < kLbMax; ++j)
+                if (lane + j * kWave < nlb) s_lbw[lane + j * kWave] = lbv[j];
+            if (!wait_ready(a.flags + (int64_t)l * kMaxLoraParts, a.lora_parts, a.epoch) && threadIdx.x == 0)
+                set_err(a.err, E0_DEV_SYNC_TIMEOUT);
+            if (threadIdx.x < 2 * a.r) s_av[threadIdx.x] = coherent_load(a.lora_a + (int64_t)l * 3 * a.r + threadIdx.x);
+            __syncthreads();
+        }
         u32x4 xr[NP][4];
         if constexpr (CHAIN) {
             // Chained: every batch's weights are requested before the wait for
@@ -1396,12 +1473,7 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *
             const int vi = lane / DUP, m = vi / kFlatBatch, rr = vi % kFlatBatch;
             const int row = row0 + bt * kFlatBatch + rr;
             float val = acc[0];
-            if (lora) {
-                const uint16_t *brow = a.lb[m] + (int64_t)l * (a.lb_ls[m] / 2) + (int64_t)row * a.r;
-                float dl = 0.0f;
-                for (int i = 0; i < a.r; ++i) dl += h2f(brow[i]) * s_av[m * a.r + i];
-                val += a.lscale * dl;
-            }
+            if (lora) val += a.lscale * lds_dot_r(s_lbw + (m * kHalfBlk + (row - row0)) * a.r, s_av + m * a.r, a.r);
             const float other = __shfl_xor(val, 32);
             if (m == 0 && lane % DUP == 0) s_hv[sub * kUnitsW + bt * kFlatBatch + rr] = silu(val) * other;
         };
@@ -1437,10 +1509,21 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *
     }
     // This wavefront's half of the h block: hi/lo fp16 pairs of h with the
     // odd pairs scaled by 1/16 (the form dot_word_m2 takes), and the half's sum.
+    if (lora && lane < a.r) {
+        // This half block's share of A_down h (its 16 hidden units, in order).
+        float p = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f16x2 a2 = as_h2(adn[j][q]);
+                p += (float)a2[0] * s_hv[8 * j + 2 * q] + (float)a2[1] * s_hv[8 * j + 2 * q + 1];
+            }
+        coherent_store(lpart(a, l) + (int64_t)(2 * c + hf) * a.r + lane, p);
+    }
     {
         const int t = lane & 15;
         const float v = s_hv[t];
-        if (lora && lane < 16) coherent_store(hrow(a, l, u) + row0 + t, v);
         const int tb = hf * 16 + t;  // element of the block
         const int p = tb % 8, j = p % 4;
         const float hv = (j & 1) ? v * 0.0625f : v;
@@ -1473,7 +1556,8 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *
 // Down rows: LPR lanes per row (d_ff = 32 * LPR), KM routed units at most
 // plus the shared expert, RW output rows per wavefront (kFuseWaves * RW per item).
 template <int LPR, int KM, int RW, bool CHAIN = false>
-E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, float *s_hsh, float *s_lora) {
+E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, float *s_part, float *s_lora,
+                            uint16_t *s_lbd) {
     constexpr int RPI = kWave / LPR;  // rows per load instruction
     constexpr int IT = RW / RPI;      // load instructions per unit
     static_assert(IT >= 1, "RW >= rows per load instruction");
@@ -1538,6 +1622,26 @@ E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, 
 #pragma unroll
     for (int k = 0; k < KM; ++k) load_unit(k, a.pool.p[6], a.pool.p[7], a.pool.p[8], slot[k], slot[k] >= 0);
     load_unit(KM, a.sh.p[6], a.sh.p[7], a.sh.p[8], 0, a.has_shared != 0);
+    // The shared expert's LoRA: B_down rows of this item's output rows, to LDS
+    // before the wait.
+    const bool lora = a.has_shared && a.r > 0;
+    if (lora) {
+        const int item_rows = kFuseWaves * RW, row_base = rb * item_rows;
+        const int n = item_rows * a.r;
+        const uint16_t *src = a.lb[2] + (int64_t)l * (a.lb_ls[2] / 2) + (int64_t)row_base * a.r;
+        constexpr int kMaxLb = (kFuseWaves * RW * kMaxR + kFuseThreads - 1) / kFuseThreads;
+        uint16_t t[kMaxLb];
+#pragma unroll
+        for (int j = 0; j < kMaxLb; ++j) {
+            const int i = threadIdx.x + j * kFuseThreads;
+            t[j] = i < n ? src[i] : (uint16_t)0;
+        }
+#pragma unroll
+        for (int j = 0; j < kMaxLb; ++j) {
+            const int i = threadIdx.x + j * kFuseThreads;
+            if (i < n) s_lbd[i] = t[j];
+        }
+    }
 
     // 2. Wait for the layer's gate/up items, then stage its h blocks (and the
     //    shared expert's fp32 h for the LoRA term).
@@ -1560,9 +1664,12 @@ E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, 
             if (i < n) reinterpret_cast<uint64_t *>(s_hb)[i] = tmp[j];
         }
     }
-    const bool lora = a.has_shared && a.r > 0;
-    if (lora)
-        for (int i = threadIdx.x; i < f; i += kFuseThreads) s_hsh[i] = coherent_load(hrow(a, l, K) + i);
+    if (lora) {
+        // The partial A_down h of every half block of the shared expert.
+        const int n = a.nch * a.r;
+        const float *src = lpart(a, l);
+        for (int i = threadIdx.x; i < n; i += kFuseThreads) s_part[i] = coherent_load(src + i);
+    }
     // Chained: the residual rows this lane group adds to, requested with the
     // staging loads (layer l - 1 finished before any gate/up item of l ran).
     float rprev[IT];
@@ -1573,13 +1680,11 @@ E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, 
     }
     __syncthreads();
     if (lora) {
-        // A_down h_shared.
-        for (int i = wv; i < a.r; i += kFuseWaves) {
-            const uint16_t *arow = a.la[2] + (int64_t)l * (a.la_ls[2] / 2) + (int64_t)i * f;
+        // A_down h_shared: the half blocks' partials summed in order.
+        if (threadIdx.x < a.r) {
             float acc = 0.0f;
-            for (int cc = lane; cc < f; cc += kWave) acc += h2f(arow[cc]) * s_hsh[cc];
-            acc = wave_sum(acc);
-            if (lane == 0) s_lora[i] = acc;
+            for (int hb = 0; hb < a.nch; ++hb) acc += s_part[hb * a.r + threadIdx.x];
+            s_lora[threadIdx.x] = acc;
         }
         __syncthreads();
     }
@@ -1618,12 +1723,7 @@ E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, 
     for (int it = 0; it < IT; ++it) {
         float v = group_sum(acc[it], LPR);
         const int row = rows0 + it;
-        if (lora) {
-            const uint16_t *brow = a.lb[2] + (int64_t)l * (a.lb_ls[2] / 2) + (int64_t)row * a.r;
-            float dl = 0.0f;
-            for (int i = 0; i < a.r; ++i) dl += h2f(brow[i]) * s_lora[i];
-            v += a.lscale * dl;
-        }
+        if (lora) v += a.lscale * lds_dot_r(s_lbd + (row - rb * (kFuseWaves * RW)) * a.r, s_lora, a.r);
         if (gl == 0) {
             a.y[(int64_t)l * d + row] = v;
             if constexpr (CHAIN) coherent_store(a.r_out + (int64_t)l * d + row, rprev[it] + v);
@@ -1635,8 +1735,9 @@ E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, 
 template <int NP, int LPR, int KM, int RW, bool CHAIN = false>
 __global__ __launch_bounds__(kFuseThreads) void decode_fused_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t s_hb[(KM + 1) * LPR * kBlk];
-    __shared__ float s_hsh[32 * LPR];
-    __shared__ float s_small[2 * kMaxR + kFuseWaves * 16];
+    __shared__ float s_part[2 * LPR * kMaxR];  // LoRA partials: d_ff / 16 half blocks x r
+    __shared__ __attribute__((aligned(16))) float s_small[2 * kMaxR + kFuseWaves * 16];
+    __shared__ __attribute__((aligned(16))) uint16_t s_lb[CHAIN ? 2 : kFuseWaves * (RW > 2 * kHalfBlk ? RW : 2 * kHalfBlk) * kMaxR];
     __shared__ __attribute__((aligned(16))) float s_rr[CHAIN ? kChainD : 4];  // chained: the layer's input residual
     // Item order: the lora items, then steps s = 0 .. L + lag - 1, step s
     // holding the gate/up items of layer s (s < L) followed by the down items
@@ -1645,7 +1746,7 @@ __global__ __launch_bounds__(kFuseThreads) void decode_fused_kernel(DecodeArgs a
     // about a machine's worth of other items to finish in.
     int item = blockIdx.x;
     if (item < a.n_lora) {
-        fused_lora_item(a, item);
+        fused_lora_item(a, item / a.lora_parts, item % a.lora_parts);
         return;
     }
     item -= a.n_lora;
@@ -1675,9 +1776,9 @@ __global__ __launch_bounds__(kFuseThreads) void decode_fused_kernel(DecodeArgs a
         else if (u < a.K)
             fused_gateup_item<NP, false>(a, l, u, cg, s_small);
         else
-            fused_gateup_item<NP, true>(a, l, u, cg, s_small);
+            fused_gateup_item<NP, true>(a, l, u, cg, s_small, nullptr, s_lb);
     } else {
-        fused_down_item<LPR, KM, RW, CHAIN>(a, l, r, s_hb, s_hsh, s_small);
+        fused_down_item<LPR, KM, RW, CHAIN>(a, l, r, s_hb, s_part, s_small, s_lb);
     }
 }
 
@@ -1737,7 +1838,7 @@ Layout decode_layout(int L, int B, int K, int E, int f, int r, int n_dn = 0) {
     o.lora = off;
     off = e0_align(off + sizeof(float) * (size_t)L * B * 3 * (r > 0 ? r : 1));
     o.flags = off;
-    off = e0_align(off + (B == 1 ? sizeof(uint64_t) * (size_t)L * (1 + (K + 1) * (size_t)(f / kHalfBlk)) : 0));
+    off = e0_align(off + (B == 1 ? sizeof(uint64_t) * (size_t)L * (kMaxLoraParts + (K + 1) * (size_t)(f / kHalfBlk)) : 0));
     o.hblk = off;
     off = e0_align(off + (B == 1 ? sizeof(uint32_t) * (size_t)L * (K + 1) * (size_t)(f / 32) * kBlk : 0));
     o.dflags = off;
@@ -1925,7 +2026,8 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
         a.epoch = e0_next_epoch();
         a.units = U;
         a.nch = f / kHalfBlk;
-        a.n_lora = (a.has_shared && r > 0) ? L : 0;
+        a.lora_parts = (2 * r + kLoraJobs - 1) / kLoraJobs;
+        a.n_lora = (a.has_shared && r > 0) ? L * a.lora_parts : 0;
         const bool small = K <= 4;
         const int rw = fused_rows_per_wave(K, lpr_f);
         const int64_t n_gu = (int64_t)U * (a.nch / kFuseWaves), n_dn = d / (kFuseWaves * rw);  // per layer
@@ -2049,6 +2151,7 @@ extern "C" e0_status e0_moe_chained_decode(const e0_moe_dims *dims, int32_t L, c
     a.units = K;
     a.nch = f / kHalfBlk;
     a.n_lora = 0;
+    a.lora_parts = 0;
     a.n_gu = (int)n_gu;
     a.n_dn = (int)n_dn;
     // Layer l's down items follow its gate/up items directly; the gate/up
