@@ -118,6 +118,89 @@ __global__ __launch_bounds__(kWave *kWaves) void prer_fc1_kernel(PrerArgs a) {
     }
 }
 
+// The same rows for d_model <= 2048 with kRowsPerWave rows per wavefront: all
+// of a wavefront's weight loads (and the hidden and the routing ids of its
+// head) are issued before any is used, so each wavefront keeps 16 KB in
+// flight instead of 4 KB.
+constexpr int kRowsPerWave = 4;
+constexpr int kSmallD = 2048;
+
+__global__ __launch_bounds__(kWave *kWaves) void prer_fc1_rows_kernel(PrerArgs a) {
+    constexpr int kC = kSmallD / 512;  // 16-byte chunks per lane of a row
+    const int lane = threadIdx.x & 63;
+    const int j = blockIdx.y;
+    const int r0 = (blockIdx.x * kWaves + wave_id()) * kRowsPerWave;
+    const int nrows = a.hid + a.E;
+    if (r0 >= nrows) return;
+    const int din = a.d + 2 * a.E;
+    const int chunks = a.d / 512;
+    // Routing id of this lane for token b (lane i < K: current id i, K + i:
+    // previous id i, else none); token 0's is requested before the weights,
+    // since its one-hot columns depend on it.
+    auto lane_id = [&](int b) {
+        int e = -1;
+        if (lane < a.K) e = a.cur[((int64_t)j * a.B + b) * a.K + lane];
+        else if (lane < 2 * a.K && a.prev) e = a.prev[((int64_t)j * a.B + b) * a.K + lane - a.K];
+        return e;
+    };
+    const int id0 = lane_id(0);
+    u32x4 w[kRowsPerWave][kC];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+        const int r = min(r0 + i, nrows - 1);
+        const bool fc1 = r < a.hid;
+        const uint16_t *row = fc1 ? reinterpret_cast<const uint16_t *>(a.fc1_w + (int64_t)j * a.fc1_ws) + (int64_t)r * din
+                                  : reinterpret_cast<const uint16_t *>(a.lin_w + (int64_t)j * a.lin_ws) + (int64_t)(r - a.hid) * a.d;
+#pragma unroll
+        for (int c = 0; c < kC; ++c)
+            w[i][c] = c < chunks ? *reinterpret_cast<const u32x4 *>(row + c * 512 + lane * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    for (int b = 0; b < a.B; ++b) {
+        const uint16_t *hv = a.h + ((int64_t)j * a.B + b) * a.d;
+        u32x4 xv[kC];
+#pragma unroll
+        for (int c = 0; c < kC; ++c)
+            xv[c] = c < chunks ? *reinterpret_cast<const u32x4 *>(hv + c * 512 + lane * 8) : u32x4{0u, 0u, 0u, 0u};
+        // This lane's one-hot column of each fc1 row (an id repeated in a
+        // row counts once: every lane compares with the earlier lanes of its
+        // list, all lanes taking part in every shuffle).
+        const int e = b == 0 ? id0 : lane_id(b);
+        const int base = lane < a.K ? 0 : a.K;
+        bool first = e >= 0 && e < a.E && lane < 2 * a.K;
+        for (int q = 0; q < a.K; ++q) {
+            const int other = __shfl(e, (base + q) & 63);
+            if (q < lane - base && other == e) first = false;
+        }
+        const int col = a.d + (lane < a.K ? 0 : a.E) + (first ? e : 0);
+        float oh[kRowsPerWave];
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) {
+            const int r = min(r0 + i, nrows - 1);
+            oh[i] = (first && r < a.hid)
+                        ? h2f(reinterpret_cast<const uint16_t *>(a.fc1_w + (int64_t)j * a.fc1_ws)[(int64_t)r * din + col])
+                        : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) {
+            const int r = r0 + i;
+            float acc = oh[i];
+#pragma unroll
+            for (int c = 0; c < kC; ++c)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_fdot2(as_h2(w[i][c][q]), as_h2(xv[c][q]), acc, false);
+            acc = wave_sum(acc);
+            if (lane == 0 && r < nrows) {
+                if (r < a.hid) {
+                    const float bias = a.fc1_b ? h2f(reinterpret_cast<const uint16_t *>(a.fc1_b + (int64_t)j * a.fc1_bs)[r]) : 0.0f;
+                    a.g[((int64_t)j * a.B + b) * a.hid + r] = gelu_erf(acc + bias);
+                } else {
+                    a.lin[((int64_t)j * a.B + b) * a.E + (r - a.hid)] = acc;
+                }
+            }
+        }
+    }
+}
+
 // o[j][b][e] = fc2[e] . g[j][b] + fc2_b[e] + lin[j][b][e]; one wavefront per row.
 __global__ __launch_bounds__(kWave *kWaves) void prer_fc2_kernel(PrerArgs a) {
     const int lane = threadIdx.x & 63;
@@ -227,7 +310,13 @@ extern "C" e0_status e0_prerouter(const e0_prerouter_heads *heads, int32_t n_hea
     a.lin = reinterpret_cast<float *>(wsb + lay.lin);
     a.out = logits_out ? logits_out : reinterpret_cast<float *>(wsb + lay.out);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(prer_fc1_kernel, dim3((hid + E + kWaves - 1) / kWaves, n_heads), dim3(kWave * kWaves), 0, st, a);
+    if (d <= kSmallD) {
+        const int per_block = kWaves * kRowsPerWave;
+        hipLaunchKernelGGL(prer_fc1_rows_kernel, dim3((hid + E + per_block - 1) / per_block, n_heads), dim3(kWave * kWaves),
+                           0, st, a);
+    } else {
+        hipLaunchKernelGGL(prer_fc1_kernel, dim3((hid + E + kWaves - 1) / kWaves, n_heads), dim3(kWave * kWaves), 0, st, a);
+    }
     if ((s = e0_launch_status())) return s;
     hipLaunchKernelGGL(prer_fc2_kernel, dim3((E + kWaves - 1) / kWaves, n_heads), dim3(kWave * kWaves), 0, st, a);
     if ((s = e0_launch_status())) return s;
