@@ -426,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
                     for (int np = 0; np < NP; ++np) {
                         const uint32_t col = (uint32_t)(np * LPR + gl);
                         const uint32_t g = col / 2;
-                        W.qv[rr][m][np] = ld128(qr[m], (uint32_t)row * (d / 2) + col * 16);
+                        W.qv[rr][m][np] = ld128_once(qr[m], (uint32_t)row * (d / 2) + col * 16);
                         W.sv[rr][m][np] = h2f(ld16(sr[m], sb_index((uint32_t)row, g, ngrp) * 2));
                         W.bv[rr][m][np] = h2f(ld16(br[m], sb_index((uint32_t)row, g, ngrp) * 2));
                     }
@@ -600,7 +600,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
                     for (int np = 0; np < NP; ++np) {
                         const uint32_t col = (uint32_t)(np * LPR + gl);  // 32-element column block
                         const uint32_t g = col / 2;                           // its group
-                        qv[rr][m][np] = ld128(qr[m], (uint32_t)row * (d / 2) + col * 16);
+                        qv[rr][m][np] = ld128_once(qr[m], (uint32_t)row * (d / 2) + col * 16);
                         sv[rr][m][np] = h2f(ld16(sr[m], sb_index((uint32_t)row, g, ngrp) * 2));
                         bv[rr][m][np] = h2f(ld16(br[m], sb_index((uint32_t)row, g, ngrp) * 2));
                     }
@@ -740,7 +740,7 @@ __global__ __launch_bounds__(kThreads, LPR <= 16 ? 3 : 1) void decode_down_kerne
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             const uint32_t row = (uint32_t)min(rows[it], d - 1);  // clamped: in-bounds, never written
-            const u32x4 qv = ld128(qb, row * (f / 2) + gl * 16);
+            const u32x4 qv = ld128_once(qb, row * (f / 2) + gl * 16);
             const float s = h2f(ld16(sb, sb_index(row, (uint32_t)g, (uint32_t)fgrp) * 2));
             const float b = h2f(ld16(bb, sb_index(row, (uint32_t)g, (uint32_t)fgrp) * 2));
             out[it] += wk * down_dot(qv, s, b, h, hsum);
@@ -805,7 +805,7 @@ __global__ __launch_bounds__(kThreads, LPR <= 16 ? 3 : 1) void decode_down_kerne
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             const uint32_t row = (uint32_t)min(rows[it], d - 1);  // clamped: in-bounds, never written
-            wr.q[it] = ld128(qb, row * (f / 2) + gl * 16);
+            wr.q[it] = ld128_once(qb, row * (f / 2) + gl * 16);
             wr.s[it] = h2f(ld16(sb, sb_index(row, (uint32_t)g, (uint32_t)fgrp) * 2));
             wr.b[it] = h2f(ld16(bb, sb_index(row, (uint32_t)g, (uint32_t)fgrp) * 2));
         }
@@ -1011,7 +1011,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_flat_kernel(DecodeArgs
 #pragma unroll
                 for (int np = 0; np < NP; ++np) {
                     const uint32_t col = (uint32_t)(np * 64 + lane);
-                    B.q[rr][m][np] = ld128(qr[m], row * (d / 2) + col * 16);
+                    B.q[rr][m][np] = ld128_once(qr[m], row * (d / 2) + col * 16);
                     const uint32_t so = sb_index(row, col / 2, (uint32_t)ngrp) * 2;
                     B.sb[rr][m][np] = (uint32_t)ld16(sr[m], so) | ((uint32_t)ld16(br[m], so) << 16);
                 }
@@ -1113,7 +1113,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_flat_kernel(DecodeArgs a
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             const uint32_t row = (uint32_t)(row0 + it * RPI + grp);
-            qv[it] = ld128(qb, row * (f / 2) + gl * 16);
+            qv[it] = ld128_once(qb, row * (f / 2) + gl * 16);
             sv[it] = h2f(ld16(sb, sb_index(row, (uint32_t)g, (uint32_t)fgrp) * 2));
             bv[it] = h2f(ld16(bb, sb_index(row, (uint32_t)g, (uint32_t)fgrp) * 2));
         }
@@ -1386,7 +1386,7 @@ E0_DEV void fused_gateup_item(const DecodeArgs &a, int l, int u, int cg, float *
                 for (int np = 0; np < NP; ++np) {
                     const uint32_t col = (uint32_t)(np * 64 + lane);
 #pragma unroll
-                    for (int rr = 0; rr < kFlatBatch; ++rr) S.q[rr][m][np] = ld128(qr[m], (r0 + rr) * (d / 2) + col * 16);
+                    for (int rr = 0; rr < kFlatBatch; ++rr) S.q[rr][m][np] = ld128_once(qr[m], (r0 + rr) * (d / 2) + col * 16);
                     const uint32_t so = sb_index(r0, col / 2, (uint32_t)ngrp) * 2;  // 4 rows inside one 8-row tile
                     const auto sv = __builtin_amdgcn_raw_buffer_load_b64(sr[m], (int)so, 0, 0);
                     const auto bv = __builtin_amdgcn_raw_buffer_load_b64(br[m], (int)so, 0, 0);
@@ -1602,7 +1602,7 @@ E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, 
             o[0] = v[0];
             o[1] = v[1];
         } else {
-            const u32x4 v = ld128(r, off);
+            const u32x4 v = ld128_once(r, off);
 #pragma unroll
             for (int j = 0; j < 4; ++j) o[j] = v[j];
         }
@@ -1614,7 +1614,7 @@ E0_DEV void fused_down_item(const DecodeArgs &a, int l, int rb, uint32_t *s_hb, 
         const rsrc_t sb = make_rsrc(part_at(ps, l, s0), on ? (uint32_t)d * fgrp * 2 : 0u);
         const rsrc_t bb = make_rsrc(part_at(pb, l, s0), on ? (uint32_t)d * fgrp * 2 : 0u);
 #pragma unroll
-        for (int it = 0; it < IT; ++it) q[u][it] = ld128(qb, (uint32_t)(rows0 + it) * (f / 2) + gl * 16);
+        for (int it = 0; it < IT; ++it) q[u][it] = ld128_once(qb, (uint32_t)(rows0 + it) * (f / 2) + gl * 16);
         const uint32_t so = sb_index((uint32_t)rows0, (uint32_t)(gl / 2), (uint32_t)fgrp) * 2;  // IT rows in one tile
         load_halves(sb, so, sv[u]);
         load_halves(bb, so, bv[u]);

@@ -65,6 +65,14 @@ E0_DEV rsrc_t make_rsrc(const void *p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcFlags);
 }
 E0_DEV u32x4 ld128(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0); }
+// The same with the nontemporal hint (cache policy bit 1), for code words a
+// call reads exactly once (the decode's expert weights): with the slot copy
+// running beside the decode, the step takes about 5% less time than with
+// the default policy.
+constexpr int kPolicyNt = 2;
+E0_DEV u32x4 ld128_once(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kPolicyNt);
+}
 E0_DEV uint16_t ld16(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0); }
 
 // A read through the constant address space: with a wave-uniform index it

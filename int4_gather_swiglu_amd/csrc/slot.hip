@@ -25,8 +25,11 @@
 //
 // Two launches: plan (one workgroup per layer: sets, compaction, tables, copy
 // list) and copy (many workgroups: 16-byte vector copies of the nine parts,
-// one linear range per expert when store and pool hold whole bundles, with
-// streaming loads and stores so the copy does not evict cached weights).
+// one linear range per expert when store and pool hold whole bundles). The
+// store's bytes are read once, with the nontemporal hint; the pool's bytes
+// are written with ordinary stores, which the next decode reads back: with
+// nontemporal stores the overlapped decode35b step measured 173 us against
+// 157 us with ordinary ones.
 #include "e0_internal.h"
 
 namespace {
@@ -197,7 +200,7 @@ E0_DEV void copy_chunk(const CopyArgs &a, int l, int i, int64_t z) {
 #pragma unroll
         for (int k = 0; k < kCopyUnits; ++k) {
             const int64_t u = u0 + (int64_t)k * kThreads + threadIdx.x;
-            if (u < n) __builtin_nontemporal_store(v[k], dst + u);
+            if (u < n) dst[u] = v[k];
         }
         return;
     }
@@ -220,7 +223,7 @@ E0_DEV void copy_chunk(const CopyArgs &a, int l, int i, int64_t z) {
     for (int k = 0; k < kCopyUnits; ++k) {
         if (dst_part[k] < 0) continue;
         u32x4 *dst = reinterpret_cast<u32x4 *>(const_cast<char *>(part_at(a.pool.p[dst_part[k]], l, slot))) + dst_off[k];
-        __builtin_nontemporal_store(v[k], dst);
+        *dst = v[k];
     }
 }
 
