@@ -61,8 +61,10 @@ def parse():
 
 
 def events(n):
-    import torch
-    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    """n pairs of timing events (device-scope release: no cache write-back for
+    the host inside the timed region)."""
+    from int4_gather_swiglu_amd.streams import Event
+    return [(Event(timing=True), Event(timing=True)) for _ in range(n)]
 
 
 def mean_ms(evs):

@@ -26,6 +26,7 @@ from __future__ import annotations
 import torch
 
 from . import _lib as E
+from .streams import Event
 
 
 class StagedPipeline:
@@ -54,14 +55,16 @@ class StagedPipeline:
                                    device=dev)
         self.main = torch.cuda.current_stream(dev)
         self.side = torch.cuda.Stream(dev) if side_stream else self.main
-        self.ev_routed = torch.cuda.Event()
-        self.ev_updated = torch.cuda.Event()
+        self.ev_routed = Event()
+        self.ev_updated = Event()
 
     # -- pieces -------------------------------------------------------------
     def side_after_main(self):
-        """Make the side stream wait for everything enqueued on main so far."""
-        self.ev_routed.record(self.main)
-        self.side.wait_event(self.ev_routed)
+        """Make the side stream wait for everything enqueued on main so far
+        (nothing to do when both are one stream)."""
+        if self.side is not self.main:
+            self.ev_routed.record(self.main)
+            self.ev_routed.wait(self.side)
 
     def route_given(self, buf: int, params: E.RouteParams, logits, fp16: bool = True, on_side: bool = False):
         """Route step logits [L][B][E] (fp16 bits or fp32) into idx/w[buf]."""
@@ -85,7 +88,8 @@ class StagedPipeline:
         else:
             E.e0_slot_update(self.dims, self.L, self.B, self.S, nxt, cur, self.slot_of, self.expert_of, self.store,
                              self.pool, self.n_copied, self.ws_slot, self.err, stream=self.side)
-        self.ev_updated.record(self.side)
+        if self.side is not self.main:
+            self.ev_updated.record(self.side)
 
     def update(self, nxt: int, cur: int | None, after_main: bool = True):
         """Slot update for idx[nxt], protecting idx[cur], on the side stream
@@ -93,7 +97,9 @@ class StagedPipeline:
         self.update_ids(self.idx[nxt], None if cur is None else self.idx[cur], after_main)
 
     def join(self):
-        self.main.wait_event(self.ev_updated)
+        """Make main wait for the last slot update on the side stream."""
+        if self.side is not self.main:
+            self.ev_updated.wait(self.main)
 
     def decode_ids(self, idx, w, x, y):
         E.e0_moe_staged_decode(self.dims, self.L, self.B, x, idx, w, self.slot_of, self.S, self.pool, self.shared, y,
