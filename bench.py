@@ -46,7 +46,8 @@ def parse():
                              "merge35b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak probes")
-    ap.add_argument("--no-overlap", action="store_true", help="run the slot update on the decode stream")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="staged workloads: the slot update in its own launches before the decode, one stream")
     ap.add_argument("--host-store", action="store_true",
                     help="keep the expert store in pinned host memory (the HBM slot pool as its cache; the slot "
                          "update pulls changed experts over the host link)")
@@ -61,7 +62,7 @@ def parse():
 
 
 def events(n):
-    """n pairs of timing events (device-scope release: no cache write-back for
+    """n pairs of timing events (no system-scope fence: no cache write-back for
     the host inside the timed region)."""
     from int4_gather_swiglu_amd.streams import Event
     return [(Event(timing=True), Event(timing=True)) for _ in range(n)]
@@ -168,14 +169,22 @@ def expert_store(args, cfg, L, Ex, bb, dev, tag=None):
 class DecodeSchedule:
     """Buffers of the staged decode workloads and the step the benchmark times.
 
-    Step t: the side stream waits for the work already on main (the decode of
-    step t - 1), routes step t + 1 and runs the slot update (next = t + 1, in
-    use = t); the main stream decodes step t; main then waits for the side
-    stream. ``pre_decode(t)``, if given, is called right before the decode of
-    step t is enqueued on main (tests put a delay there to widen the window in
-    which the side stream rewrites slots)."""
+    Step t: the side stream waits for main's decode of step t - 1
+    (recorded right after it, so the side does not also wait for main's wait
+    on the side), routes step t + 1 and runs the slot update; the main stream
+    decodes step t; main then waits for the side stream. The side stream thus
+    routes and plans step t + 1 while main is still waiting for the copies of
+    step t, before the decode of step t occupies the machine.
+    --no-overlap: the routing and slot update, then the decode, on one stream.
+    ``pre_decode(t)`` / ``post_decode(t)``, if given, are called right before
+    and right after the decode of step t is enqueued on main (tests put a delay
+    before it, to widen the window in which the side stream rewrites slots, and
+    checks of the slots it reads on both sides of it); ``post_update(t,
+    stream)`` right after the slot update for step t + 1 is enqueued, with the
+    stream it is on (tests read the slot tables there: the next update may
+    start before main's wait for this one ends)."""
 
-    def __init__(self, args, cfg, n_in, chain=False, pre_decode=None):
+    def __init__(self, args, cfg, n_in, chain=False, pre_decode=None, post_decode=None, post_update=None):
         import torch
 
         from e0inputs import gen, workloads as W
@@ -184,7 +193,8 @@ class DecodeSchedule:
 
         dev = torch.device("cuda:0")
         L, B, K, Ex, S, d, f = cfg.L, cfg.B, cfg.K, cfg.E, args.hot_slots or cfg.S, cfg.d, cfg.f
-        self.cfg, self.n_in, self.chain, self.pre_decode = cfg, n_in, chain, pre_decode
+        self.cfg, self.n_in, self.chain = cfg, n_in, chain
+        self.pre_decode, self.post_decode, self.post_update = pre_decode, post_decode, post_update
         self.L, self.B, self.K, self.Ex, self.S, self.d, self.f = L, B, K, Ex, S, d, f
         self.bb = bb = gen.bundle_bytes(d, f)
         # The full expert store filled on the GPU; per-step inputs drawn on the
@@ -223,13 +233,15 @@ class DecodeSchedule:
     def step(self, t, rec):
         pipe = self.pipe
         nb, cb = (t + 1) % 2, t % 2
-        pipe.side_after_main()
+        pipe.side_after_decode()
         if rec is not None:
             self.ev_upd[rec][0].record(pipe.side)
         self.route(nb, t + 1, True)
         pipe.update(nb, cb, after_main=False)
         if rec is not None:
             self.ev_upd[rec][1].record(pipe.side)
+        if self.post_update is not None:
+            self.post_update(t, pipe.side)
         if self.pre_decode is not None:
             self.pre_decode(t)
         if rec is not None:
@@ -240,6 +252,9 @@ class DecodeSchedule:
             pipe.decode(cb, self.xs[t % self.n_in], self.y)
         if rec is not None:
             self.ev_dec[rec][1].record(pipe.main)
+        if self.post_decode is not None:
+            self.post_decode(t)
+        pipe.mark_decoded()
         pipe.join()
 
 
@@ -262,17 +277,30 @@ def bench_decode(args, cfg, n_in, chain=False):
     uniq, copies = [], []
     for s in range(min(n_in, 16)):
         route(s % 2, s, False)
-        pipe.update(s % 2, (s - 1) % 2 if s else None, after_main=False)
+        pipe.update(s % 2, (s - 1) % 2 if s else None)  # after the routing on main
         pipe.join()
         torch.cuda.synchronize()
         ids = pipe.idx[s % 2].cpu().numpy().reshape(L, -1)
         uniq.append(np.mean([len(np.unique(r)) for r in ids]))
         if s:
             copies.append(int(pipe.n_copied.sum().item()))
+    # The decode alone (nothing beside it), outside the timed region: the
+    # routing of the last replayed step, median of 20 calls.
+    last = (min(n_in, 16) - 1) % 2
+    ev_alone = events(20)
+    for a_, b_ in ev_alone:
+        a_.record(pipe.main)
+        if chain:
+            pipe.decode_chain(last, sch.r_ins[0], sch.norm_w, CHAIN_EPS, sch.y, sch.r_out)
+        else:
+            pipe.decode(last, sch.xs[0], sch.y)
+        b_.record(pipe.main)
+    torch.cuda.synchronize()
+    alone_ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in ev_alone]))
     dec_ms, upd_ms = mean_ms(ev_dec), mean_ms(ev_upd)
     algo_bytes = int(round(L * float(np.mean(uniq)) * bb))
-    achieved = algo_bytes / (dec_ms * 1e-3) / 1e9
     copy_bytes = int(round(2 * float(np.mean(copies)) * bb)) if copies else 0
+    achieved = algo_bytes / (dec_ms * 1e-3) / 1e9
     step_s = wall / args.steps
     return dict(value=round(args.steps * B / wall, 2), unit=f"tok/s ({L}-layer MoE stack, batch {B})",
                 ms_per_step=round(wall * 1e3 / args.steps, 5),
@@ -283,6 +311,11 @@ def bench_decode(args, cfg, n_in, chain=False):
                         "layers": L, "experts": Ex, "d_model": d, "d_ff": f, "top_k": K, "batch": B, "slots": S},
                 layer_tok_per_s=round(args.steps * B * L / wall, 1),
                 decode_call_us=round(dec_ms * 1e3, 2), route_and_slot_update_us=round(upd_ms * 1e3, 2),
+                decode_alone={"us": round(alone_ms * 1e3, 2), "bytes": algo_bytes,
+                              "achieved": round(algo_bytes / (alone_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                              "frac": round(algo_bytes / (alone_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "note": "the decode call with nothing beside it, outside the timed region, median of "
+                                      "20"},
                 slot_copies_per_step=round(float(np.mean(copies)), 2) if copies else 0.0, overlap=not args.no_overlap,
                 step_hbm={"bytes_per_step": algo_bytes + copy_bytes, "decode_bytes": algo_bytes,
                           "slot_copy_bytes": copy_bytes,
@@ -628,10 +661,11 @@ class PrerouterSchedule:
     t + 1 overlap step t's compute. The slot update waits for the decode of
     step t - 1 (it may evict that step's experts); the decode of step t + 1
     waits for the update (join). Routing state R[t % 3] is [L+1][1][K] (row
-    0: the unstaged owner of head 0). ``pre_decode(t)`` as in DecodeSchedule.
+    0: the unstaged owner of head 0). ``pre_decode(t)``, ``post_decode(t)``,
+    ``post_update(t, stream)`` as in DecodeSchedule.
     ``inputs`` (a workloads.Prerouted) replaces the drawn inputs if given."""
 
-    def __init__(self, args, cfg, n_in, pre_decode=None, inputs=None):
+    def __init__(self, args, cfg, n_in, pre_decode=None, inputs=None, post_decode=None, post_update=None):
         import torch
 
         from e0inputs import gen, gpu as G, workloads as W
@@ -640,7 +674,8 @@ class PrerouterSchedule:
 
         dev = torch.device("cuda:0")
         L, K, Ex, S, d, f = cfg.L, cfg.K, cfg.E, args.hot_slots or cfg.S, cfg.d, cfg.f
-        self.cfg, self.n_in, self.pre_decode = cfg, n_in, pre_decode
+        self.cfg, self.n_in = cfg, n_in
+        self.pre_decode, self.post_decode, self.post_update = pre_decode, post_decode, post_update
         self.L, self.K, self.Ex, self.S, self.d, self.f = L, K, Ex, S, d, f
         self.bb = bb = gen.bundle_bytes(d, f)
 
@@ -687,7 +722,9 @@ class PrerouterSchedule:
         pipe.predict(self.hin[t % n_in], R[c], R[p] if t > 0 else None, R[n], Wt[n], on_side=True)
         if rec is not None:
             self.ev_pre[rec][1].record(pipe.side)
-        pipe.update_ids(R[n, 1:], R[c, 1:])
+        pipe.update_ids(R[n, 1:], R[c, 1:], after_decode=True)
+        if self.post_update is not None:
+            self.post_update(t, pipe.side)
         if self.pre_decode is not None:
             self.pre_decode(t)
         if rec is not None:
@@ -695,6 +732,9 @@ class PrerouterSchedule:
         pipe.decode_ids(R[c, 1:], Wt[c, 1:], self.hin[t % n_in, 1:], self.y)
         if rec is not None:
             self.ev_dec[rec][1].record(pipe.main)
+        if self.post_decode is not None:
+            self.post_decode(t)
+        pipe.mark_decoded()
         pipe.join()
 
 

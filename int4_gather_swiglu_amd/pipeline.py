@@ -5,7 +5,8 @@ Per step t (fixed double-buffered slots, routing ids kept on the GPU; the
 update for step t+1 overlaps step t: koala.ai.kr paths table and Fig. 1
 timeline; jaehun.me review, report 3.1):
 
-  side : waits for the work already on main (decode t-1 read idx[(t+1) % 2])
+  side : waits for main's decode of step t-1 (it read idx[(t+1) % 2] and the
+         slots the update may rewrite), not for main's wait on the side
   side : routing of step t+1          -> idx[(t+1) % 2]   (e0_route)
   side : slot update                  next = idx[(t+1) % 2], in use = idx[t % 2]
   main : staged decode of step t      reads idx[t % 2] through the slot table
@@ -57,6 +58,8 @@ class StagedPipeline:
         self.side = torch.cuda.Stream(dev) if side_stream else self.main
         self.ev_routed = Event()
         self.ev_updated = Event()
+        self.ev_decoded = Event()  # recorded on main right after each decode
+        self._decoded = False
 
     # -- pieces -------------------------------------------------------------
     def side_after_main(self):
@@ -65,6 +68,23 @@ class StagedPipeline:
         if self.side is not self.main:
             self.ev_routed.record(self.main)
             self.ev_routed.wait(self.side)
+
+    def side_after_decode(self):
+        """Make the side stream wait for main's work up to the last
+        mark_decoded (a decode), not for what main enqueued after it, such as
+        its wait for the side stream's last update: the next update's plan and
+        copies only need the decode of the step before the one in flight to
+        have finished."""
+        if self.side is not self.main and self._decoded:
+            self.ev_decoded.wait(self.side)
+
+    def mark_decoded(self):
+        """Record main's work so far (a decode, and whatever the caller put on
+        main after it that must also precede the next update) as what the next
+        side_after_decode waits for."""
+        if self.side is not self.main:
+            self.ev_decoded.record(self.main)
+            self._decoded = True
 
     def route_given(self, buf: int, params: E.RouteParams, logits, fp16: bool = True, on_side: bool = False):
         """Route step logits [L][B][E] (fp16 bits or fp32) into idx/w[buf]."""
@@ -76,9 +96,13 @@ class StagedPipeline:
         E.e0_route(params, self.L, self.B, self.dims.n_experts, None, False, x, w_router, self.dims.d_model,
                    self.idx[buf], self.w[buf], logits_out, stream=self.side if on_side else self.main)
 
-    def update_ids(self, nxt, cur, after_main: bool = True):
-        """Slot update for routing ids `nxt` [L][B][K], protecting `cur` (or None)."""
-        if after_main:
+    def update_ids(self, nxt, cur, after_main: bool = True, after_decode: bool = False):
+        """Slot update for routing ids `nxt` [L][B][K], protecting `cur` (or
+        None), on the side stream: after everything enqueued on main so far
+        (after_main), or after main's last decode only (after_decode)."""
+        if after_decode:
+            self.side_after_decode()
+        elif after_main:
             self.side_after_main()
         if self.hot_set:
             E.e0_slot_update_lru(self.dims, self.L, self.B, self.S, nxt, cur, self.slot_of, self.expert_of,

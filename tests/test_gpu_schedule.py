@@ -14,7 +14,8 @@ decode, so the side stream's slot update for step t + 1 has finished before
 the decode of step t starts: an update that rewrote a slot step t reads would
 show in that step's output. They also compare, on the main stream just before
 and just after each decode, the pool bytes of every slot step t reads with the
-store's bytes of the expert it should hold."""
+store's bytes of the expert it should hold (the check after a decode is
+enqueued before the side stream may start the next update)."""
 import argparse
 from concurrent.futures import ThreadPoolExecutor
 
@@ -58,6 +59,26 @@ def _hazard_hook(T, delay, state, checks):
     return pre
 
 
+def _tables_hook(T, pipe_of, tabs):
+    """Slot tables right after the update for step t + 1, copied on the stream
+    the update ran on (the update for t + 2 may start before main has waited
+    for this one)."""
+    def hook(t, stream):
+        pipe = pipe_of()
+        with T.cuda.stream(stream):
+            tabs.append((pipe.slot_of.clone(), pipe.expert_of.clone()))
+    return hook
+
+
+def _post_hook(state, post):
+    """Right after the decode of step t on main (before the next update may
+    start): the slots step t read still hold its experts' bytes."""
+    def hook(t):
+        s = state["sch"]
+        post.append(_resident_ok(s.pipe, s.store, s.pool, state["idx"](t)))
+    return hook
+
+
 def _replay(E, S, routes, L):
     """Oracle slot rule over routes[s] ([L][K] per step); tables after each update."""
     so = np.full((L, E), -1, np.int32)
@@ -91,20 +112,19 @@ def test_decode35b_bench_schedule(delay):
     T = U.torch()
     cfg = W.DECODE35
     L, K = cfg.L, cfg.K
-    checks, state = [], {}
-    sch = bench.DecodeSchedule(_args(STEPS), cfg, STEPS, pre_decode=_hazard_hook(T, delay, state, checks))
+    checks, state, post, tabs = [], {}, [], []
+    sch = bench.DecodeSchedule(_args(STEPS), cfg, STEPS, pre_decode=_hazard_hook(T, delay, state, checks),
+                               post_decode=_post_hook(state, post),
+                               post_update=_tables_hook(T, lambda: state["sch"].pipe, tabs))
     state["sch"] = sch
     state["idx"] = lambda t: sch.pipe.idx[t % 2]
     pipe = sch.pipe
     rec = [dict(idx=pipe.idx[0].clone(), w=pipe.w[0].clone())]
-    tabs, ys, post = [], [], []
+    ys = []
     for t in range(STEPS):
         sch.step(t, None)
-        # on the main stream, after step t (main has joined the side stream)
-        post.append(_resident_ok(pipe, sch.store, sch.pool, pipe.idx[t % 2]))
         ys.append(sch.y.clone())
         rec.append(dict(idx=pipe.idx[(t + 1) % 2].clone(), w=pipe.w[(t + 1) % 2].clone()))
-        tabs.append((pipe.slot_of.clone(), pipe.expert_of.clone()))
     T.cuda.synchronize()
     assert int(pipe.err.item()) == 0
     assert all(bool(c.item()) for c in checks), "a slot read by a step held other bytes before its decode"
@@ -142,19 +162,18 @@ def test_prerouted35b_bench_schedule(delay):
     P = W.prerouted_inputs(cfg, STEPS)
     heads = [W.head(cfg, j) for j in range(L)]
     lor = [W.lora(cfg, l) for l in range(L)]
-    checks, state = [], {}
+    checks, state, post, tabs = [], {}, [], []
     sch = bench.PrerouterSchedule(_args(STEPS), cfg, STEPS, pre_decode=_hazard_hook(T, delay, state, checks),
-                                  inputs=P)
+                                  inputs=P, post_decode=_post_hook(state, post),
+                                  post_update=_tables_hook(T, lambda: state["sch"].pipe, tabs))
     state["sch"] = sch
     state["idx"] = lambda t: sch.R[t % 3, 1:]
     pipe = sch.pipe
-    preds, tabs, ys, post = [], [], [], []
+    preds, ys = [], []
     for t in range(STEPS):
         sch.step(t, None)
-        post.append(_resident_ok(pipe, sch.store, sch.pool, sch.R[t % 3, 1:]))
         ys.append(sch.y.clone())
         preds.append((sch.R[(t + 1) % 3].clone(), sch.Wt[(t + 1) % 3].clone()))
-        tabs.append((pipe.slot_of.clone(), pipe.expert_of.clone()))
     T.cuda.synchronize()
     assert int(pipe.err.item()) == 0
     assert all(bool(c.item()) for c in checks) and all(bool(c.item()) for c in post)
