@@ -660,8 +660,11 @@ class PrerouterSchedule:
     earlier: the one-token lead lets the prediction and the staging of step
     t + 1 overlap step t's compute. The slot update waits for the decode of
     step t - 1 (it may evict that step's experts); the decode of step t + 1
-    waits for the update (join). Routing state R[t % 3] is [L+1][1][K] (row
-    0: the unstaged owner of head 0). ``pre_decode(t)``, ``post_decode(t)``,
+    waits for the update (join). Routing state R[t % n] (a ring of n >= 3
+    steps, n a multiple of n_in, r_of(t)) is [L+1][1][K]; row 0, the unstaged owner of head 0,
+    is an input of every step and is filled for the whole ring up front. The
+    views each step passes are built once (the step is otherwise bound by
+    the host's Python work). ``pre_decode(t)``, ``post_decode(t)``,
     ``post_update(t, stream)`` as in DecodeSchedule.
     ``inputs`` (a workloads.Prerouted) replaces the drawn inputs if given."""
 
@@ -702,34 +705,44 @@ class PrerouterSchedule:
                                              E.stack_from_bundles(pool, d, f, bb, S * bb), E.heads_from_tensors(*hd_t),
                                              E.route_params(0, K), shared=shared, device=dev,
                                              side_stream=not args.no_overlap, hot_set=bool(args.hot_slots))
-        self.R = R = torch.zeros((3, L + 1, 1, K), dtype=torch.int32, device=dev)
-        self.Wt = torch.full((3, L + 1, 1, K), 1.0 / K, dtype=torch.float32, device=dev)
-        R[0, 0, 0] = self.owner0[0]
+        self.nr = nr = n_in * ((3 + n_in - 1) // n_in)  # at least 3 slots, a multiple of n_in
+        self.R = R = torch.zeros((nr, L + 1, 1, K), dtype=torch.int32, device=dev)
+        self.Wt = torch.full((nr, L + 1, 1, K), 1.0 / K, dtype=torch.float32, device=dev)
+        for i in range(nr):
+            R[i, 0, 0] = self.owner0[i % n_in]
         R[0, 1:, 0] = torch.from_numpy(P.r0).to(dev)
         self.y = torch.empty((L, 1, d), dtype=torch.float32, device=dev)
         self.ev_dec, self.ev_pre = events(args.steps), events(args.steps)
+        # Views of each ring slot and input step, made once.
+        self.vR = [R[i] for i in range(nr)]
+        self.vR1 = [R[i, 1:] for i in range(nr)]
+        self.vW = [self.Wt[i] for i in range(nr)]
+        self.vW1 = [self.Wt[i, 1:] for i in range(nr)]
+        self.vh = [self.hin[i] for i in range(n_in)]
+        self.vh1 = [self.hin[i, 1:] for i in range(n_in)]
         pipe.update_ids(R[0, 1:], None)
         pipe.join()
 
+    def r_of(self, t):
+        """Ring slot of step t's routing state."""
+        return t % self.nr
+
     def step(self, t, rec):
-        import torch
-        pipe, R, Wt, n_in = self.pipe, self.R, self.Wt, self.n_in
-        c, n, p = t % 3, (t + 1) % 3, (t - 1) % 3
-        with torch.cuda.stream(pipe.side):
-            R[n, 0, 0].copy_(self.owner0[(t + 1) % n_in])
+        pipe, nr, i = self.pipe, self.nr, t % self.n_in
+        c, n, p = t % nr, (t + 1) % nr, (t - 1) % nr
         if rec is not None:
             self.ev_pre[rec][0].record(pipe.side)
-        pipe.predict(self.hin[t % n_in], R[c], R[p] if t > 0 else None, R[n], Wt[n], on_side=True)
+        pipe.predict(self.vh[i], self.vR[c], self.vR[p] if t > 0 else None, self.vR[n], self.vW[n], on_side=True)
         if rec is not None:
             self.ev_pre[rec][1].record(pipe.side)
-        pipe.update_ids(R[n, 1:], R[c, 1:], after_decode=True)
+        pipe.update_ids(self.vR1[n], self.vR1[c], after_decode=True)
         if self.post_update is not None:
             self.post_update(t, pipe.side)
         if self.pre_decode is not None:
             self.pre_decode(t)
         if rec is not None:
             self.ev_dec[rec][0].record(pipe.main)
-        pipe.decode_ids(R[c, 1:], Wt[c, 1:], self.hin[t % n_in, 1:], self.y)
+        pipe.decode_ids(self.vR1[c], self.vW1[c], self.vh1[i], self.y)
         if rec is not None:
             self.ev_dec[rec][1].record(pipe.main)
         if self.post_decode is not None:

@@ -167,13 +167,13 @@ def test_prerouted35b_bench_schedule(delay):
                                   inputs=P, post_decode=_post_hook(state, post),
                                   post_update=_tables_hook(T, lambda: state["sch"].pipe, tabs))
     state["sch"] = sch
-    state["idx"] = lambda t: sch.R[t % 3, 1:]
+    state["idx"] = lambda t: sch.R[sch.r_of(t), 1:]
     pipe = sch.pipe
     preds, ys = [], []
     for t in range(STEPS):
         sch.step(t, None)
         ys.append(sch.y.clone())
-        preds.append((sch.R[(t + 1) % 3].clone(), sch.Wt[(t + 1) % 3].clone()))
+        preds.append((sch.R[sch.r_of(t + 1)].clone(), sch.Wt[sch.r_of(t + 1)].clone()))
     T.cuda.synchronize()
     assert int(pipe.err.item()) == 0
     assert all(bool(c.item()) for c in checks) and all(bool(c.item()) for c in post)
