@@ -779,8 +779,9 @@ __global__ __launch_bounds__(kThreads, LPR <= 16 ? 3 : 1) void decode_down_kerne
     // expert's pairs in token order), each pair's contribution folded into the
     // block's per-token accumulators in that order. The h rows of a chunk of
     // pairs are staged in LDS by one cooperative load (their latencies
-    // overlap), and the weight rows of the next pair are requested before the
-    // current pair is computed.
+    // overlap). An expert's pairs form one run: its weight rows are loaded
+    // once for the run, and the next expert's rows are requested when a run
+    // starts, so their latency hides behind the whole run.
     for (int i = threadIdx.x; i < a.B * kDownRows; i += kThreads) s_acc[i / kDownRows][i % kDownRows] = 0.0f;
     __syncthreads();
     const int nu = a.ucnt[l];
@@ -814,10 +815,17 @@ __global__ __launch_bounds__(kThreads, LPR <= 16 ? 3 : 1) void decode_down_kerne
     const int chunk = kHChunkFloats / f;  // pairs per LDS chunk (f <= 2048: at least 2)
     const int32_t *pslot = a.pslot + (int64_t)l * a.B * a.K;
     const float *wl = a.w + (int64_t)l * a.B * a.K;
+    const int32_t *uslot = a.uslot + (int64_t)l * a.umax;
+    auto uslot_at = [&](int u) {
+        const int sl = cload(uslot, u);
+        return sl < 0 ? 0 : sl;  // a non-resident expert's pairs are skipped below; its load reads slot 0
+    };
     Wrows wc, wn;
-    if (npairs > 0) {
-        const int s0 = cload(pslot, 0);
-        load_w(s0 < 0 ? 0 : s0, wc);
+    int u_cur = 0, run_end = 0;  // the current run's expert and the pair after its run
+    if (nu > 0) {
+        load_w(uslot_at(0), wc);
+        run_end = cload(uoff, 1);
+        if (nu > 1) load_w(uslot_at(1), wn);
     }
     for (int c0 = 0; c0 < npairs; c0 += chunk) {
         const int cn = min(chunk, npairs - c0);
@@ -862,9 +870,12 @@ __global__ __launch_bounds__(kThreads, LPR <= 16 ? 3 : 1) void decode_down_kerne
         __syncthreads();
         for (int pc = 0; pc < cn; ++pc) {
             const int pi = c0 + pc;
-            if (pi + 1 < npairs) {
-                const int sn = s_pslot[pc + 1];
-                load_w(sn < 0 ? 0 : sn, wn);
+            if (pi == run_end && u_cur + 1 < nu) {
+                // The next expert's run starts: its rows were requested a run ago.
+                ++u_cur;
+                wc = wn;
+                run_end = cload(uoff, u_cur + 1);
+                if (u_cur + 1 < nu) load_w(uslot_at(u_cur + 1), wn);
             }
             if (s_pslot[pc] >= 0) {
                 uint32_t hh[16], hl[16];
@@ -891,7 +902,6 @@ __global__ __launch_bounds__(kThreads, LPR <= 16 ? 3 : 1) void decode_down_kerne
                 }
                 fold(part, s_pid[pc] / a.K);
             }
-            wc = wn;
         }
     }
     if (a.has_shared) {
