@@ -466,11 +466,12 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
                     xs[t][np] = sm;
                 }
             }
-            Wb Wc, Wn;
-            load_rows(row_base, Wc);
-            for (int gi = 0; gi < G; ++gi) {
+            // Two register stages used in turn (group gi computes from one
+            // while group gi + 1's rows land in the other), so no copy.
+            Wb W0, W1;
+            load_rows(row_base, W0);
+            auto group = [&](int gi, const Wb &Wc, Wb &Wn) {
                 const int rbase = row_base + gi * ROWS_B;
-                if (rbase >= a.f) break;
                 if (gi + 1 < G) load_rows(rbase + ROWS_B, Wn);
                 float acc[NVc];
 #pragma unroll
@@ -517,7 +518,13 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
                     if (m == 0 && (NVc >= LPR || gl % DUP == 0) && row < a.f && tok[t] >= 0)
                         hrow(a, l, pid[t])[row] = silu(val) * other;
                 }
-                Wc = Wn;
+            };
+            static_assert(G % 2 == 0, "groups are taken in pairs");
+            for (int gi = 0; gi < G; gi += 2) {
+                if (row_base + gi * ROWS_B >= a.f) break;
+                group(gi, W0, W1);
+                if (row_base + (gi + 1) * ROWS_B >= a.f) break;
+                group(gi + 1, W1, W0);
             }
         };
         for (int c0 = 0; c0 < p_count;) {
