@@ -77,7 +77,8 @@ struct DecodeArgs {
     int32_t *uoff;   // [L][umax + 1]
     int32_t *pairs;  // [L][B*K]
     int32_t *pslot;  // [L][B*K] slot of the expert of each sorted pair (-1: not resident)
-    float *hbuf;     // [L][B*K + B][f]
+    float *pwt;      // [L][B*K] routing weight of each sorted pair
+    float *hbuf;     // [L][B*K + B][f]: B == 1 k order; B > 1 sorted pair order; then the shared expert's
     float *lora_a;   // [L][B][3][r]
     uint32_t *hblk;  // [L][units][d_ff / 32][kBlk] (single-launch batch-1 path)
     // single-launch batch-1 path
@@ -204,6 +205,7 @@ __global__ __launch_bounds__(kThreads) void decode_prep_kernel(DecodeArgs a) {
             for (int q = 0; q < p; ++q) rank += s_ids[q] == e;
             pairs[s_base[e] + rank] = p;
             a.pslot[(int64_t)l * n + s_base[e] + rank] = s_slot[e];
+            a.pwt[(int64_t)l * n + s_base[e] + rank] = a.w[(int64_t)l * n + p];
         }
     }
 
@@ -448,8 +450,8 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
                         tk = ci;
                         p = a.B * a.K + ci;
                     } else {
-                        p = plist[p_begin + ci];
-                        tk = p / a.K;
+                        tk = plist[p_begin + ci] / a.K;
+                        p = p_begin + ci;  // a batch keeps its h rows in sorted pair order
                     }
                 }
                 tok[t] = tk;
@@ -557,8 +559,8 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(DecodeArgs a) {
                     tk = ci;
                     p = a.B * a.K + ci;
                 } else if (plist) {
-                    p = plist[p_begin + ci];
-                    tk = p / a.K;
+                    tk = plist[p_begin + ci] / a.K;
+                    p = p_begin + ci;  // a batch keeps its h rows in sorted pair order
                 } else {
                     p = p_begin;
                     tk = 0;
@@ -858,7 +860,7 @@ __global__ __launch_bounds__(kThreads, LPR <= 16 ? 3 : 1) void decode_down_kerne
         uint32_t *s_hq = reinterpret_cast<uint32_t *>(s_h);
         for (int v = threadIdx.x; v < cn * LPR * 4; v += kThreads) {
             const int pc = v / (LPR * 4), gq = (v / 4) % LPR, wd = v % 4;
-            const float *src = hrow(a, l, plist[c0 + pc]) + gq * 32 + wd * 8;
+            const float *src = hrow(a, l, c0 + pc) + gq * 32 + wd * 8;
             const f32x4 lo4 = *reinterpret_cast<const f32x4 *>(src), hi4 = *reinterpret_cast<const f32x4 *>(src + 4);
             u32x4 qh, ql;
 #pragma unroll
@@ -932,6 +934,325 @@ __global__ __launch_bounds__(kThreads, LPR <= 16 ? 3 : 1) void decode_down_kerne
             v += a.lscale * dl;
         }
         a.y[((int64_t)l * a.B + t) * d + row] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3b. down for B > 1 on the matrix cores (v_mfma_f32_16x16x32_f16), d_ff of
+// 128, 256 or 512. A block owns kDownRows output rows of a layer, 16 per wavefront, and
+// walks the layer's experts in sorted order, then the shared expert. The MFMA
+// rows are a window of 16 consecutive sorted pairs, staged in LDS as fp16
+// hi + lo parts of h in the order of the denormal-nibble product (pairs
+// (h_j, h_j+4) per code word, odd j scaled by 1/16); the columns are the
+// wavefront's 16 output rows, with their code words as fp16 denormals
+// (q 2^-24, exact); each product is exact in fp32. Per quantisation group g
+// (64 inputs: two K = 32 slices, hi and lo) P_g = 2^-24 sum q h, and the
+// group adds s 2^24 P_g + b sum_g h. A pass computes all 16 rows of the
+// window and folds those of the current expert, times their routing weight,
+// into the block's per-token accumulators in LDS in sorted order (y written
+// once, no atomics). The experts' weight rows (16 code bytes per lane per two
+// groups, and the wavefront's scales and biases, 8 rows of one group per
+// lane, in one 16-byte load) sit in a ring of kDmRing register stages: expert
+// u + kDmRing - 1 is requested before expert u is computed.
+// Lane (n = lane % 16, kq = lane / 16): A row n = window slot n, B column
+// n = output row n, over inputs 32 (kq & 1) + 8 (kq >> 1) + 16 s .. + 7 of
+// group g for the slices s = 0, 1; C rows 4 kq .. 4 kq + 3 (window slots) of
+// column n.
+// ---------------------------------------------------------------------------
+constexpr int kDmSlots = 16;  // window slots (MFMA rows)
+constexpr int kDmRing = 4;    // weight stages in flight
+
+typedef _Float16 h8mf __attribute__((ext_vector_type(8)));
+typedef float f4mf __attribute__((ext_vector_type(4)));
+
+// Code word w (8 codes) as the B operand: (q0, q4, 16 q1, 16 q5, q2, q6,
+// 16 q3, 16 q7) x 2^-24 as fp16 denormals.
+E0_DEV h8mf nib_operand(uint32_t w) {
+    const uint32_t w8 = w >> 8;
+    const u32x4 t = {w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
+    return __builtin_bit_cast(h8mf, t);
+}
+
+template <int FG>
+struct DmStage {
+    u32x4 w[FG / 2];  // chunk c: 16 code bytes of output row n at byte 64 c + 16 kq (group 2 c + kq / 2)
+    u32x4 sb;         // lane i < 2 FG: scales of 8 rows of one group; lane 32 + i: the biases
+};
+
+// Dynamic LDS of the kernel (bytes): accumulators, LoRA A h, h window, group
+// sums of the window, each wavefront's scale/bias table, and the layer's run
+// table (first pair of each expert's run, and its slot).
+__host__ __device__ inline int dm_slot_dwords(int fg) { return fg * 64 + 4; }  // + 16 B: slots start on different banks
+__host__ __device__ inline size_t dm_lds_bytes(int B, int r, int fg, int umax) {
+    return (size_t)4 * (B * kDownRows + ((B * r + 3) & ~3) + kDmSlots * dm_slot_dwords(fg) + fg * kDmSlots) +
+           (size_t)kWaves * 512 + (size_t)4 * (2 * umax + 1);
+}
+constexpr size_t kDmMaxLds = 64 * 1024;
+
+// Every global load of the expert loop is unconditional and the same for
+// every expert (the ring's tail re-reads the last expert), so the compiler
+// can count the loads issued after a stage and wait for that stage alone
+// instead of for all loads in flight.
+template <int FG>
+__global__ __launch_bounds__(kThreads, 3) void decode_down_mfma_kernel(DecodeArgs a) {
+    extern __shared__ __attribute__((aligned(16))) float dm_lds[];
+    __shared__ int s_tok[kDmSlots];
+    __shared__ float s_wt[kDmSlots];
+    const int lane = threadIdx.x & 63, wv = wave_id(), tid = threadIdx.x;
+    const int nl = lane & 15, kq = lane >> 4;
+    const int l = blockIdx.x, row0 = blockIdx.y * kDownRows;
+    const int d = a.d, f = FG * kGroup, B = a.B;
+    constexpr int slot_dw = FG * 64 + 4;
+    float *s_acc = dm_lds;                      // [B][kDownRows]
+    float *s_lora = s_acc + B * kDownRows;      // [B][r]
+    uint32_t *s_hw = reinterpret_cast<uint32_t *>(s_lora + ((B * a.r + 3) & ~3));  // [slot][g][kq][hi w0, hi w1, lo w0, lo w1]
+    float *s_hs = reinterpret_cast<float *>(s_hw + kDmSlots * slot_dw);          // [g][slot]
+    uint16_t *s_sb0 = reinterpret_cast<uint16_t *>(s_hs + FG * kDmSlots);
+    uint16_t *s_sb = s_sb0 + wv * 256;  // [s|b][octet][g][8 rows]
+    int32_t *s_uoff = reinterpret_cast<int32_t *>(s_sb0 + kWaves * 256);  // [umax + 1]
+    int32_t *s_uslot = s_uoff + a.umax + 1;                               // [umax]
+
+    // Shared-expert LoRA: a_d[t] = A_down h_shared[t] (r values per token).
+    const bool lora = a.has_shared && a.r > 0;
+    if (lora) {
+        const int jobs = B * a.r;
+        for (int job = wv; job < jobs; job += kWaves) {
+            const int t = job / a.r, i = job % a.r;
+            const uint16_t *arow = a.la[2] + (int64_t)l * (a.la_ls[2] / 2) + (int64_t)i * f;
+            const float *hs = hrow(a, l, B * a.K + t);
+            float acc = 0.0f;
+            for (int c = lane; c < f; c += kWave) acc += h2f(arow[c]) * hs[c];
+            acc = wave_sum(acc);
+            if (lane == 0) s_lora[t * a.r + i] = acc;
+        }
+    }
+    for (int i = tid; i < B * kDownRows; i += kThreads) s_acc[i] = 0.0f;
+
+    const int row = row0 + wv * 16 + nl;
+    const uint32_t rowc = (uint32_t)min(row, d - 1);  // clamped: in-bounds, never written
+    const int nu = a.ucnt[l];
+    const int nrun = nu + (a.has_shared ? 1 : 0);
+    const int32_t *uoff = a.uoff + (int64_t)l * (a.umax + 1);
+    const int32_t *uslot = a.uslot + (int64_t)l * a.umax;
+    const int32_t *plist = a.pairs + (int64_t)l * B * a.K;
+    const float *pwt = a.pwt + (int64_t)l * B * a.K;
+    const int npairs = nu > 0 ? cload(uoff, nu) : 0;
+    // The run table in LDS: the expert loop reads it in a few cycles where a
+    // scalar load from memory would put a round trip in front of every run.
+    for (int i = tid; i <= nu; i += kThreads) s_uoff[i] = uoff[i];
+    for (int i = tid; i < nu; i += kThreads) s_uslot[i] = uslot[i];
+    const int ntot = npairs + (a.has_shared ? B : 0);
+    // This lane's 16-byte chunk of the wavefront's scale (lanes 0-31) or bias
+    // (lanes 32-63) rows: octet oct0 + i / FG, group i % FG (i = lane mod
+    // 2 FG; the lanes past 2 FG repeat a chunk and are not used).
+    const int li = lane & 31;
+    const int sbi = li % (2 * FG);
+    const uint32_t sb_off = (uint32_t)((min((row0 + wv * 16) / 8 + sbi / FG, d / 8 - 1) * FG + sbi % FG) * 16);
+
+    auto load_stage = [&](int u, DmStage<FG> &S) {
+        u = min(u, nrun - 1);
+        const bool shx = u >= nu;
+        int slot = 0;
+        if (!shx) {
+            slot = __builtin_amdgcn_readfirstlane(s_uslot[u]);
+            slot = slot < 0 ? 0 : slot;  // a non-resident expert is skipped; its stage reads slot 0
+        }
+        const Part pq = shx ? a.sh.p[6] : a.pool.p[6];
+        const Part ps = shx ? a.sh.p[7] : a.pool.p[7];
+        const Part pb = shx ? a.sh.p[8] : a.pool.p[8];
+        const rsrc_t qb = make_rsrc(part_at(pq, l, slot), (uint32_t)d * f / 2);
+        // Each load reads 64 contiguous bytes (two groups) of each of the 16
+        // rows: a probe of this grid streams that pattern at the full read
+        // rate, and 32 bytes of 16 rows per load at three quarters of it.
+        // One offset register for the stage's loads (the chunk goes in the
+        // instruction's immediate offset), not one per chunk held by the
+        // loop. Plain loads: with the nontemporal hint the wavefronts stalled
+        // about twice as long issuing them.
+        uint32_t qoff = rowc * (f / 2) + kq * 16;
+        __asm__ volatile("" : "+v"(qoff));
+#pragma unroll
+        for (int c = 0; c < FG / 2; ++c) S.w[c] = __builtin_amdgcn_raw_buffer_load_b128(qb, (int)(qoff + c * 64), 0, 0);
+        const char *sbp = lane < 32 ? part_at(ps, l, slot) : part_at(pb, l, slot);
+        S.sb = *reinterpret_cast<const u32x4 *>(sbp + sb_off);
+    };
+
+    // Window c: slots c * 16 .. c * 16 + 15 of the sorted pairs (then the
+    // shared expert's B rows). Every wavefront takes part. The window's rows
+    // and routing data are requested before the barrier that frees the LDS,
+    // so the two waits overlap.
+    constexpr int kItems = kDmSlots * FG * 4;  // (slot, group, quarter): 16 h values each
+    constexpr int kIpt = (kItems + kThreads - 1) / kThreads;
+    int cur = -1;
+    auto stage_window = [&](int c) {
+        float v[kIpt][16];
+#pragma unroll
+        for (int k = 0; k < kIpt; ++k) {
+            const int it = tid + k * kThreads;
+            const int q4 = it & 3, g = (it >> 2) % FG, sl = (it >> 2) / FG;
+            const int pi = c * kDmSlots + sl;
+            if (it < kItems && pi < ntot) {
+                const int hp = pi < npairs ? pi : B * a.K + (pi - npairs);
+                // the inputs lane kq = q4 takes in the pass: 8 at 32 (q4 & 1) +
+                // 8 (q4 >> 1) + 16 s of the group, s = 0, 1
+                const float *src = hrow(a, l, hp) + g * kGroup + 32 * (q4 & 1) + 8 * (q4 >> 1);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 t = *reinterpret_cast<const f32x4 *>(src + 16 * (j >> 1) + 4 * (j & 1));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[k][4 * j + e] = t[e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) v[k][e] = 0.0f;
+            }
+        }
+        int tk = -1;
+        float wt = 0.0f;
+        if (tid < kDmSlots) {
+            const int pi = c * kDmSlots + tid;
+            if (pi < npairs) {
+                tk = plist[pi] / a.K;
+                wt = pwt[pi];
+            } else if (pi < ntot) {
+                tk = pi - npairs;
+                wt = 1.0f;
+            }
+        }
+        __syncthreads();  // every wavefront is done with the previous window
+#pragma unroll
+        for (int k = 0; k < kIpt; ++k) {
+            const int it = tid + k * kThreads;
+            if (it < kItems) {
+                const int q4 = it & 3, g = (it >> 2) % FG, sl = (it >> 2) / FG;
+                u32x4 hv[2], lv[2];
+                float sum = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float sc = (e & 1) ? 0.0625f : 1.0f;
+                        const float va = v[k][8 * j + e] * sc, vb = v[k][8 * j + e + 4] * sc;
+                        const f16 ha = (f16)va, hb = (f16)vb;
+                        const f16 la = (f16)(va - (float)ha), lb = (f16)(vb - (float)hb);
+                        hv[j][e] = (uint32_t)__builtin_bit_cast(uint16_t, ha) | (uint32_t)__builtin_bit_cast(uint16_t, hb) << 16;
+                        lv[j][e] = (uint32_t)__builtin_bit_cast(uint16_t, la) | (uint32_t)__builtin_bit_cast(uint16_t, lb) << 16;
+                        sum += v[k][8 * j + e] + v[k][8 * j + e + 4];
+                    }
+                }
+                u32x4 *dst = reinterpret_cast<u32x4 *>(s_hw + sl * slot_dw + (g * 4 + q4) * 16);
+                dst[0] = hv[0];
+                dst[1] = hv[1];
+                dst[2] = lv[0];
+                dst[3] = lv[1];
+                // the four quarters of a group are four consecutive lanes
+                sum += __shfl_xor(sum, 1);
+                sum += __shfl_xor(sum, 2);
+                if (q4 == 0) s_hs[g * kDmSlots + sl] = sum;
+            }
+        }
+        if (tid < kDmSlots) {
+            s_tok[tid] = tk;
+            s_wt[tid] = wt;
+        }
+        __syncthreads();
+    };
+
+    // One expert against window slots [sa, sb).
+    auto pass = [&](const DmStage<FG> &S, int sa, int sb) {
+        if (li < 2 * FG) *reinterpret_cast<u32x4 *>(s_sb + (((lane >> 5) * 2 + li / FG) * 8 + li % FG) * 8) = S.sb;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint32_t *hb = s_hw + nl * slot_dw + kq * 16;
+        const int so = (nl >> 3) * 64 + (nl & 7);
+        f4mf tot = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int g = 0; g < FG; ++g) {
+            const u32x4 *hq = reinterpret_cast<const u32x4 *>(hb + g * 64);
+            // Chunk g / 2 holds group g / 2 * 2 in lanes 0-31 and the next
+            // group in lanes 32-63. Swapping the upper lanes of words 0 and 2
+            // with the lower lanes of words 1 and 3 gives two registers
+            // holding only the first group (codes 32 (kq & 1) + 8 (kq >> 1)
+            // + 16 s, s = 0, 1) and two holding only the second, in the same
+            // lane order.
+            const u32x4 W = S.w[g >> 1];
+            const auto r01 = __builtin_amdgcn_permlane32_swap(W[0], W[1], false, false);
+            const auto r23 = __builtin_amdgcn_permlane32_swap(W[2], W[3], false, false);
+            // The code words pass through an empty asm so that their masks
+            // are formed here, per group, not hoisted out of the expert's
+            // passes (that would hold 64 more registers).
+            uint32_t w0 = r01[g & 1], w1 = r23[g & 1];
+            __asm__ volatile("" : "+v"(w0), "+v"(w1));
+            const h8mf b0 = nib_operand(w0), b1 = nib_operand(w1);
+            f4mf P = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8mf, hq[0]), b0,
+                                                           f4mf{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            P = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8mf, hq[1]), b1, P, 0, 0, 0);
+            P = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8mf, hq[2]), b0, P, 0, 0, 0);
+            P = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8mf, hq[3]), b1, P, 0, 0, 0);
+            const float sc = h2f(s_sb[so + g * 8]) * kDenormScale, bi = h2f(s_sb[128 + so + g * 8]);
+            const f4mf hs4 = *reinterpret_cast<const f4mf *>(s_hs + g * kDmSlots + 4 * kq);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tot[i] = __builtin_fmaf(sc, P[i], __builtin_fmaf(bi, hs4[i], tot[i]));
+            // formed here, group by group: sunk into the fold's branches, the
+            // sums would hold every group's products and operands at once
+            __asm__ volatile("" : "+v"(tot));
+        }
+        if (row < d) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int sl = 4 * kq + i;
+                if (sl >= sa && sl < sb) s_acc[s_tok[sl] * kDownRows + (row - row0)] += s_wt[sl] * tot[i];
+            }
+        }
+        __builtin_amdgcn_wave_barrier();  // the table is rewritten by the next pass
+    };
+
+    auto run = [&](int u, const DmStage<FG> &S) {
+        const int p0 = u < nu ? __builtin_amdgcn_readfirstlane(s_uoff[u]) : npairs;
+        const int p1 = u < nu ? __builtin_amdgcn_readfirstlane(s_uoff[u + 1]) : ntot;
+        const bool ok = u >= nu || __builtin_amdgcn_readfirstlane(s_uslot[u]) >= 0;
+        for (int p = p0; p < p1;) {
+            const int c = p / kDmSlots;
+            while (cur < c) stage_window(++cur);
+            const int q = min(p1, (c + 1) * kDmSlots);
+            if (ok) pass(S, p - c * kDmSlots, q - c * kDmSlots);
+            p = q;
+        }
+    };
+
+    __syncthreads();  // run table, LoRA terms and zeroed accumulators
+    if (nrun > 0) {
+        static_assert(kDmRing == 4, "the ring below is unrolled for four stages");
+        DmStage<FG> S0, S1, S2, S3;
+        load_stage(0, S0);
+        load_stage(1, S1);
+        load_stage(2, S2);
+        for (int u = 0; u < nrun; u += kDmRing) {
+            load_stage(u + 3, S3);
+            run(u, S0);
+            if (u + 1 >= nrun) break;
+            load_stage(u + 4, S0);
+            run(u + 1, S1);
+            if (u + 2 >= nrun) break;
+            load_stage(u + 5, S1);
+            run(u + 2, S2);
+            if (u + 3 >= nrun) break;
+            load_stage(u + 6, S2);
+            run(u + 3, S3);
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < B * kDownRows; i += kThreads) {
+        const int t = i / kDownRows, rr = i % kDownRows, orow = row0 + rr;
+        if (orow >= d) continue;
+        float v = s_acc[i];
+        if (lora) {
+            const uint16_t *brow = a.lb[2] + (int64_t)l * (a.lb_ls[2] / 2) + (int64_t)orow * a.r;
+            float dl = 0.0f;
+            for (int j = 0; j < a.r; ++j) dl += h2f(brow[j]) * s_lora[t * a.r + j];
+            v += a.lscale * dl;
+        }
+        a.y[((int64_t)l * B + t) * d + orow] = v;
     }
 }
 
@@ -1821,7 +2142,7 @@ int d_lpr(int d, int &np) {
 int f_lpr(int f) { return (f >= 128 && f <= 2048 && pow2(f)) ? f / 32 : 0; }
 
 struct Layout {
-    size_t ucnt, uexp, uslot, uoff, pairs, pslot, hbuf, lora, flags, hblk, dflags, total;
+    size_t ucnt, uexp, uslot, uoff, pairs, pslot, pwt, hbuf, lora, flags, hblk, dflags, total;
 };
 
 // Output rows per wavefront of a down item of the single-launch kernel: at
@@ -1850,6 +2171,8 @@ Layout decode_layout(int L, int B, int K, int E, int f, int r, int n_dn = 0) {
     off = e0_align(off + sizeof(int32_t) * (size_t)L * B * K);
     o.pslot = off;
     off = e0_align(off + sizeof(int32_t) * (size_t)L * B * K);
+    o.pwt = off;
+    off = e0_align(off + sizeof(float) * (size_t)L * B * K);
     o.hbuf = off;
     off = e0_align(off + sizeof(float) * (size_t)L * (B * K + B) * f);
     o.lora = off;
@@ -2029,6 +2352,7 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
     a.uoff = reinterpret_cast<int32_t *>(wsb + lay.uoff);
     a.pairs = reinterpret_cast<int32_t *>(wsb + lay.pairs);
     a.pslot = reinterpret_cast<int32_t *>(wsb + lay.pslot);
+    a.pwt = reinterpret_cast<float *>(wsb + lay.pwt);
     a.hbuf = reinterpret_cast<float *>(wsb + lay.hbuf);
     a.lora_a = reinterpret_cast<float *>(wsb + lay.lora);
     a.flags = reinterpret_cast<uint64_t *>(wsb + lay.flags);
@@ -2112,6 +2436,19 @@ extern "C" e0_status e0_moe_staged_decode(const e0_moe_dims *dims, int32_t L, in
         E0_REQUIRE(ok, E0_ERR_UNSUPPORTED_SHAPE);
     }
     if ((s = e0_launch_status())) return s;
+    if (B > 1) {
+        // Batches at d_ff = 128, 256 or 512: the matrix-core down kernel.
+        const dim3 grid(L, (d + kDownRows - 1) / kDownRows);
+        const size_t lds = dm_lds_bytes(B, r, f / kGroup, a.umax);
+        bool mf = lds <= kDmMaxLds;
+        switch (mf ? f / kGroup : 0) {
+            case 2: hipLaunchKernelGGL(decode_down_mfma_kernel<2>, grid, dim3(kThreads), lds, st, a); break;
+            case 4: hipLaunchKernelGGL(decode_down_mfma_kernel<4>, grid, dim3(kThreads), lds, st, a); break;
+            case 8: hipLaunchKernelGGL(decode_down_mfma_kernel<8>, grid, dim3(kThreads), lds, st, a); break;
+            default: mf = false;
+        }
+        if (mf) return e0_launch_status();
+    }
     E0_REQUIRE(dispatch_down(lpr_f, a, dim3(L, (d + kDownRows - 1) / kDownRows), st), E0_ERR_UNSUPPORTED_SHAPE);
     return e0_launch_status();
 }
