@@ -1165,38 +1165,42 @@ __global__ __launch_bounds__(kThreads, 3) void decode_down_mfma_kernel(DecodeArg
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const uint32_t *hb = s_hw + nl * slot_dw + kq * 16;
         const int so = (nl >> 3) * 64 + (nl & 7);
-        f4mf tot = {0.0f, 0.0f, 0.0f, 0.0f};
+        // The nibble masks and shift pass through an empty asm so that the
+        // code words' masks are formed in this pass, group by group, not
+        // hoisted out of the expert's passes (that would hold 64 more
+        // registers).
+        uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, sh8 = 8;
+        __asm__ volatile("" : "+v"(m_lo), "+v"(m_hi), "+v"(sh8));
+        f4mf totp = {0.0f, 0.0f, 0.0f, 0.0f}, totb = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int g = 0; g < FG; ++g) {
             const u32x4 *hq = reinterpret_cast<const u32x4 *>(hb + g * 64);
-            // Chunk g / 2 holds group g / 2 * 2 in lanes 0-31 and the next
-            // group in lanes 32-63. Swapping the upper lanes of words 0 and 2
-            // with the lower lanes of words 1 and 3 gives two registers
-            // holding only the first group (codes 32 (kq & 1) + 8 (kq >> 1)
-            // + 16 s, s = 0, 1) and two holding only the second, in the same
-            // lane order.
+            // words (s = 0, 1) of group g: word 2 s + (g & 1) of the swapped chunk
             const u32x4 W = S.w[g >> 1];
-            const auto r01 = __builtin_amdgcn_permlane32_swap(W[0], W[1], false, false);
-            const auto r23 = __builtin_amdgcn_permlane32_swap(W[2], W[3], false, false);
-            // The code words pass through an empty asm so that their masks
-            // are formed here, per group, not hoisted out of the expert's
-            // passes (that would hold 64 more registers).
-            uint32_t w0 = r01[g & 1], w1 = r23[g & 1];
-            __asm__ volatile("" : "+v"(w0), "+v"(w1));
-            const h8mf b0 = nib_operand(w0), b1 = nib_operand(w1);
+            const uint32_t w0 = W[g & 1], w1 = W[2 + (g & 1)], w08 = w0 >> sh8, w18 = w1 >> sh8;
+            const h8mf b0 = __builtin_bit_cast(h8mf, u32x4{w0 & m_lo, w0 & m_hi, w08 & m_lo, w08 & m_hi});
+            const h8mf b1 = __builtin_bit_cast(h8mf, u32x4{w1 & m_lo, w1 & m_hi, w18 & m_lo, w18 & m_hi});
             f4mf P = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8mf, hq[0]), b0,
                                                            f4mf{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
             P = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8mf, hq[1]), b1, P, 0, 0, 0);
             P = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8mf, hq[2]), b0, P, 0, 0, 0);
             P = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8mf, hq[3]), b1, P, 0, 0, 0);
-            const float sc = h2f(s_sb[so + g * 8]) * kDenormScale, bi = h2f(s_sb[128 + so + g * 8]);
+            // s P_g and b sum_g h kept apart (the 2^24 of the products is
+            // applied once, below), each with the fp16 factor taken as is
+            const float sc = h2f(s_sb[so + g * 8]), bi = h2f(s_sb[128 + so + g * 8]);
             const f4mf hs4 = *reinterpret_cast<const f4mf *>(s_hs + g * kDmSlots + 4 * kq);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) tot[i] = __builtin_fmaf(sc, P[i], __builtin_fmaf(bi, hs4[i], tot[i]));
+            for (int i = 0; i < 4; ++i) {
+                totp[i] = __builtin_fmaf(sc, P[i], totp[i]);
+                totb[i] = __builtin_fmaf(bi, hs4[i], totb[i]);
+            }
             // formed here, group by group: sunk into the fold's branches, the
             // sums would hold every group's products and operands at once
-            __asm__ volatile("" : "+v"(tot));
+            __asm__("" : "+v"(totp), "+v"(totb));
         }
+        f4mf tot;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tot[i] = __builtin_fmaf(kDenormScale, totp[i], totb[i]);
         if (row < d) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1207,7 +1211,26 @@ __global__ __launch_bounds__(kThreads, 3) void decode_down_mfma_kernel(DecodeArg
         __builtin_amdgcn_wave_barrier();  // the table is rewritten by the next pass
     };
 
-    auto run = [&](int u, const DmStage<FG> &S) {
+    // Chunk c holds group 2 c in lanes 0-31 and group 2 c + 1 in lanes 32-63.
+    // Swapping the upper lanes of words 0 and 2 with the lower lanes of words
+    // 1 and 3 leaves words 0 and 2 holding only group 2 c (codes 32 (kq & 1) +
+    // 8 (kq >> 1) + 16 s, s = 0, 1) and words 1 and 3 only group 2 c + 1, in
+    // the same lane order. Done once per expert, in place (the stage is not
+    // read again until it is reloaded).
+    auto swap_stage = [&](const DmStage<FG> &S) {
+        DmStage<FG> T;
+#pragma unroll
+        for (int c = 0; c < FG / 2; ++c) {
+            const auto r01 = __builtin_amdgcn_permlane32_swap(S.w[c][0], S.w[c][1], false, false);
+            const auto r23 = __builtin_amdgcn_permlane32_swap(S.w[c][2], S.w[c][3], false, false);
+            T.w[c] = u32x4{r01[0], r01[1], r23[0], r23[1]};
+        }
+        T.sb = S.sb;
+        return T;
+    };
+
+    auto run = [&](int u, const DmStage<FG> &S0_) {
+        const DmStage<FG> S = swap_stage(S0_);
         const int p0 = u < nu ? __builtin_amdgcn_readfirstlane(s_uoff[u]) : npairs;
         const int p1 = u < nu ? __builtin_amdgcn_readfirstlane(s_uoff[u + 1]) : ntot;
         const bool ok = u >= nu || __builtin_amdgcn_readfirstlane(s_uslot[u]) >= 0;
