@@ -1,6 +1,6 @@
 """GPU parity of the batched (B > 1) staged decode at the 8B tier's expert shape
 (d_model 2048, d_ff 512): a ragged number of sorted pairs (20, not a multiple of
-the 8-pair h chunk the down kernel stages in LDS), experts holding 6, 4, 3, 2
+the 16-pair h window the down kernel stages in LDS), experts holding 6, 4, 3, 2
 and 1 tokens (gate/up token chunks of 4, 2 and 1, one with a padding slot), an
 id out of range and an expert with no slot. Every token is checked against the
 fp64 oracle's staged path, which skips the same contributions, and the device
