@@ -987,7 +987,7 @@ __host__ __device__ inline size_t dm_lds_bytes(int B, int r, int fg, int umax) {
     return (size_t)4 * (B * kDownRows + ((B * r + 3) & ~3) + kDmSlots * dm_slot_dwords(fg) + fg * kDmSlots) +
            (size_t)kWaves * 512 + (size_t)4 * (2 * umax + 1);
 }
-constexpr size_t kDmMaxLds = 64 * 1024;
+constexpr size_t kDmMaxLds = 64 * 1024 - 256;  // dynamic LDS cap, leaving room for the static arrays
 
 // Every global load of the expert loop is unconditional and the same for
 // every expert (the ring's tail re-reads the last expert), so the compiler
