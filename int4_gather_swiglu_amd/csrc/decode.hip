@@ -965,14 +965,6 @@ constexpr int kDmRing = 4;    // weight stages in flight
 typedef _Float16 h8mf __attribute__((ext_vector_type(8)));
 typedef float f4mf __attribute__((ext_vector_type(4)));
 
-// Code word w (8 codes) as the B operand: (q0, q4, 16 q1, 16 q5, q2, q6,
-// 16 q3, 16 q7) x 2^-24 as fp16 denormals.
-E0_DEV h8mf nib_operand(uint32_t w) {
-    const uint32_t w8 = w >> 8;
-    const u32x4 t = {w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
-    return __builtin_bit_cast(h8mf, t);
-}
-
 template <int FG>
 struct DmStage {
     u32x4 w[FG / 2];  // chunk c: 16 code bytes of output row n at byte 64 c + 16 kq (group 2 c + kq / 2)
@@ -1177,6 +1169,8 @@ __global__ __launch_bounds__(kThreads, 3) void decode_down_mfma_kernel(DecodeArg
             const u32x4 *hq = reinterpret_cast<const u32x4 *>(hb + g * 64);
             // words (s = 0, 1) of group g: word 2 s + (g & 1) of the swapped chunk
             const u32x4 W = S.w[g >> 1];
+            // a code word w (8 codes) as the B operand: (q0, q4, 16 q1, 16 q5,
+            // q2, q6, 16 q3, 16 q7) x 2^-24 as fp16 denormals
             const uint32_t w0 = W[g & 1], w1 = W[2 + (g & 1)], w08 = w0 >> sh8, w18 = w1 >> sh8;
             const h8mf b0 = __builtin_bit_cast(h8mf, u32x4{w0 & m_lo, w0 & m_hi, w08 & m_lo, w08 & m_hi});
             const h8mf b1 = __builtin_bit_cast(h8mf, u32x4{w1 & m_lo, w1 & m_hi, w18 & m_lo, w18 & m_hi});
