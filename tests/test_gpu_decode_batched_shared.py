@@ -1,7 +1,7 @@
 """GPU parity of the batched (B > 1) staged decode with the shared expert and
 its unmerged LoRA, at d_model 2048 with d_ff 256, 512 and 1024 (the matrix-core
 down kernel at 256 and 512, the vector down kernel at 1024), and at d_model
-1024 and 4096 (other gate/up lane layouts), on a workspace
+1024 and 4096 (other gate/up lane layouts), and at the largest batch (64), on a workspace
 filled with 0xFF bytes before the call (no stale h row may reach an output).
 Every token of every layer against the fp64 oracle: the routed experts'
 staged sum plus the shared expert with its LoRA terms."""
@@ -22,9 +22,10 @@ def E():
     return _lib
 
 
-@pytest.mark.parametrize("d,f", [(2048, 256), (2048, 512), (2048, 1024), (1024, 128), (4096, 512)])
-def test_batched_decode_shared_expert_with_lora(d, f):
-    cfg = W.scaled(W.PREROUTED35, E=24, L=2, B=5, d=d, f=f, shared_f=f)
+@pytest.mark.parametrize("d,f,B", [(2048, 256, 5), (2048, 512, 5), (2048, 1024, 5), (1024, 128, 5), (4096, 512, 5),
+                                   (2048, 512, 64)])
+def test_batched_decode_shared_expert_with_lora(d, f, B):
+    cfg = W.scaled(W.PREROUTED35, E=24, L=2, B=B, d=d, f=f, shared_f=f)
     L, B, K, d = cfg.L, cfg.B, cfg.K, cfg.d
     from e0inputs import gpu as G
     store = U.gpu_store(cfg, range(L))
