@@ -790,6 +790,7 @@ def bench_prerouted(args, cfg, n_in):
 # ---------------------------------------------------------------------------
 
 TRAFFIC_SOURCES = {"decode35b": ("int4_gather_swiglu_amd/csrc/decode.hip", "int4_gather_swiglu_amd/csrc/e0_internal.h"),
+                   "decode8b_b32": ("int4_gather_swiglu_amd/csrc/decode.hip", "int4_gather_swiglu_amd/csrc/e0_internal.h"),
                    "prefill35b": ("int4_gather_swiglu_amd/csrc/prefill.hip", "int4_gather_swiglu_amd/csrc/e0_internal.h")}
 
 
