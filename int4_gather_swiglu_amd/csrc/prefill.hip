@@ -19,11 +19,15 @@
 //  3. gemm2    (tiles x d_model/256): Yb[pair] = w_pair * (H D^T).
 //  4. combine  : y[t] = sum over k in order of Yb[t*K + k].
 // The last M-tile of an expert runs only the 32-row MFMA blocks that hold
-// rows. Tiles are dealt to the eight XCDs round robin, heaviest first.
+// rows; a tile of at most 16 rows (the popularity tail) runs its own path.
+// Tiles are dealt to the eight XCDs, heaviest first.
 //
 // MFMA v_mfma_f32_32x32x16_f16 on fp16 operands. A rows go from global memory
 // straight into LDS; B fragments are code words dequantised in registers (one
 // fp16 fma per weight, a single rounding of the exact dequantised value).
+// Tiles of at most 16 rows: v_mfma_f32_16x16x32_f16 with the code words as
+// exact fp16 denormals, the group scale applied to the products in fp32 and
+// the bias as a product of the rows' group sums with the biases.
 #include "e0_internal.h"
 
 #include <math.h>
@@ -451,6 +455,221 @@ E0_DEV void prefill_tile(const PrefillArgs &a, uint16_t (*s_a)[kTM * kARow], int
     }
 }
 
+// ---------------------------------------------------------------------------
+// Tiles of at most 16 rows: most active experts of a layer receive only a
+// few of its pairs (the popularity tail), and a 32-row block would compute
+// padding while every weight of the tile is still dequantised. Here the
+// matrix cores take v_mfma_f32_16x16x32_f16 with the code words themselves
+// as the B operand, fp16 denormals q 2^-24 (exact), so no weight is
+// dequantised: the two MFMAs of quantisation group g give P_g = 2^-24
+// sum_k q_k x_k for 16 rows x 16 columns, and the group adds s_g 2^24 P_g
+// (one fma per output). The bias part, sum_g b_g sum_{k in g} x_k, is itself
+// a product over the groups: the rows' group sums X (fp32, as fp16 hi + lo)
+// against the fp16 biases, two MFMAs per 32 groups after the main loop.
+// Every product is exact in fp32; the dequantised weight s q + b is never
+// rounded to fp16 (the 128-row tiles round it once).
+//
+// Lane (n = lane % 16, kq = lane / 16): A row n, B column n (the wavefront's
+// output column 16 cb + n), over inputs 32 (kq & 1) + 8 (kq >> 1) + 16 s .. + 7
+// of group g for the slices s = 0, 1; C rows 4 kq .. 4 kq + 3 of column n.
+// A code word (8 codes, the lowest nibble first) becomes (q0, q4, 16 q1,
+// 16 q5, q2, q6, 16 q3, 16 q7) x 2^-24 by one shift and four masks; the rows
+// are staged in LDS in the same order, the positions of 16 q scaled by 1/16
+// (exact for |x| >= 2^-10; below that the fp16 quotient is subnormal and keeps
+// fewer bits). Each lane loads 16 bytes of its column per 128-input step (64
+// contiguous bytes per column: group 2 st in lanes 0-31, 2 st + 1 in lanes
+// 32-63); two lane swaps leave registers that each hold one group.
+constexpr int kSmallRowPad = 136;     // halves per staged row: 16 chunks + one (rows start on other banks)
+constexpr int kSmallMaxGroups = 256;  // group sums kept in LDS (reduction length up to 16384)
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// (x_j, x_{j+4}) pairs of 8 consecutive fp16 values in the MFMA order above,
+// the pairs that meet 16 q scaled by 1/16.
+E0_DEV u32x4 small_a_chunk(u32x4 x) {
+    const f16x2 k16 = f16x2{(f16)0.0625f, (f16)0.0625f};
+    u32x4 o;
+    o[0] = __builtin_amdgcn_perm(x[2], x[0], 0x05040100u);
+    o[1] = __builtin_bit_cast(uint32_t, as_h2(__builtin_amdgcn_perm(x[2], x[0], 0x07060302u)) * k16);
+    o[2] = __builtin_amdgcn_perm(x[3], x[1], 0x05040100u);
+    o[3] = __builtin_bit_cast(uint32_t, as_h2(__builtin_amdgcn_perm(x[3], x[1], 0x07060302u)) * k16);
+    return o;
+}
+
+// A code word as the B operand: (q0, q4, 16 q1, 16 q5, q2, q6, 16 q3, 16 q7) x 2^-24.
+E0_DEV h8 small_b_word(uint32_t w) {
+    const uint32_t w8 = w >> 8;
+    return __builtin_bit_cast(h8, u32x4{w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u});
+}
+
+template <int NB, bool GATEUP>
+E0_DEV void prefill_small_tile(const PrefillArgs &a, uint16_t (*s_a)[kTM * kARow], int e, int m0, int m_end, int nt) {
+    constexpr int kCols = 4 * 32 * (GATEUP ? 1 : NB);
+    constexpr int kNcb = GATEUP ? 4 : 2 * NB;  // 16-column blocks per wavefront (gate/up: gate 0-1, up 2-3)
+    constexpr int kMats = GATEUP ? 2 : 1;
+    constexpr float kDenorm = 16777216.0f;    // 2^24
+    const int Kdim = GATEUP ? a.d : a.f;
+    const int Nall = GATEUP ? a.f : a.d;
+    const int ngroups = Kdim / kGroup;
+    const int nsteps = Kdim / kStepK;
+    const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+    const int nl = lane & 15, kq = lane >> 4;
+
+    uint16_t *sA = &s_a[0][0];                                      // [2][16][kSmallRowPad]
+    float *sX = reinterpret_cast<float *>(sA + 2 * 16 * kSmallRowPad);  // [16][ngroups] group sums
+
+    // Staging: thread tid takes chunk c = tid % 16 (inputs 8 c .. 8 c + 7 of
+    // the step) of row r = tid / 16. Rows past the tile load row m0 and stage
+    // zeros.
+    const int sr_ = tid >> 4, sc_ = tid & 15;
+    const bool aok = m0 + sr_ < m_end;
+    const int arow = GATEUP ? a.perm[aok ? m0 + sr_ : m0] / a.K : (aok ? m0 + sr_ : m0);
+    const uint16_t *asrc = (GATEUP ? a.x : a.H) + (int64_t)arow * Kdim + 8 * sc_;
+    const int scc = sc_ & 7, sg = sc_ >> 3;
+    const int sslot = ((sg * 4 + ((scc >> 2) | ((scc & 1) << 1))) * 2 + ((scc >> 1) & 1)) * 8;
+    auto stage_a = [&](int st, int buf, u32x4 x) {
+        if (!aok) x = u32x4{0u, 0u, 0u, 0u};
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f16x2 p = as_h2(x[i]);
+            sum += (float)p[0] + (float)p[1];
+        }
+        // the 8 chunks of one (row, group) are 8 consecutive lanes
+        sum += __shfl_xor(sum, 1);
+        sum += __shfl_xor(sum, 2);
+        sum += __shfl_xor(sum, 4);
+        if (scc == 0) sX[sr_ * ngroups + 2 * st + sg] = sum;
+        *reinterpret_cast<u32x4 *>(sA + (buf * 16 + sr_) * kSmallRowPad + sslot) = small_a_chunk(x);
+    };
+
+    rsrc_t qr[kMats], sr[kMats], br[kMats];
+#pragma unroll
+    for (int mi = 0; mi < kMats; ++mi) {
+        const int pm = GATEUP ? mi : 2;
+        qr[mi] = make_rsrc(part_at(a.layer.p[3 * pm + 0], 0, e), (uint32_t)Nall * Kdim / 2);
+        sr[mi] = make_rsrc(part_at(a.layer.p[3 * pm + 1], 0, e), (uint32_t)Nall * ngroups * 2);
+        br[mi] = make_rsrc(part_at(a.layer.p[3 * pm + 2], 0, e), (uint32_t)Nall * ngroups * 2);
+    }
+    uint32_t col[kNcb];
+#pragma unroll
+    for (int cb = 0; cb < kNcb; ++cb)
+        col[cb] = GATEUP ? nt * kCols + wv * 32 + (cb & 1) * 16 + nl : nt * kCols + wv * 32 * NB + cb * 16 + nl;
+    auto mat = [](int cb) { return GATEUP ? cb >> 1 : 0; };
+
+    struct Stage {
+        u32x4 w[kNcb];
+        uint32_t s[kNcb][2];
+    };
+    auto fetch = [&](int st, Stage &S) {
+#pragma unroll
+        for (int cb = 0; cb < kNcb; ++cb) {
+            S.w[cb] = ld128(qr[mat(cb)], col[cb] * (uint32_t)(Kdim / 2) + st * 64 + kq * 16);
+#pragma unroll
+            for (int g = 0; g < 2; ++g) S.s[cb][g] = ld16(sr[mat(cb)], sb_index(col[cb], 2 * st + g, ngroups) * 2);
+        }
+    };
+
+    f4v tot[kNcb];
+#pragma unroll
+    for (int cb = 0; cb < kNcb; ++cb) tot[cb] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto compute = [&](int buf, const Stage &S) {
+        u32x4 W[kNcb];
+#pragma unroll
+        for (int cb = 0; cb < kNcb; ++cb) {
+            const auto r01 = __builtin_amdgcn_permlane32_swap(S.w[cb][0], S.w[cb][1], false, false);
+            const auto r23 = __builtin_amdgcn_permlane32_swap(S.w[cb][2], S.w[cb][3], false, false);
+            W[cb] = u32x4{r01[0], r01[1], r23[0], r23[1]};  // word 2 s + g: slice s of group g
+        }
+        const uint16_t *arow_l = sA + (buf * 16 + nl) * kSmallRowPad + kq * 16;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const h8 a0 = *reinterpret_cast<const h8 *>(arow_l + g * 64);
+            const h8 a1 = *reinterpret_cast<const h8 *>(arow_l + g * 64 + 8);
+#pragma unroll
+            for (int cb = 0; cb < kNcb; ++cb) {
+                f4v P = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, small_b_word(W[cb][g]), f4v{0.0f, 0.0f, 0.0f, 0.0f},
+                                                               0, 0, 0);
+                P = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, small_b_word(W[cb][2 + g]), P, 0, 0, 0);
+                const float sc = h2f((uint16_t)S.s[cb][g]) * kDenorm;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tot[cb][i] = __builtin_fmaf(sc, P[i], tot[cb][i]);
+            }
+        }
+    };
+
+    // Step st: request the rows and weights of step st + 1, compute step st
+    // from LDS buffer st & 1, wait, stage the next rows, barrier.
+    Stage cur, nxt;
+    fetch(0, cur);
+    u32x4 av = *reinterpret_cast<const u32x4 *>(asrc);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    stage_a(0, 0, av);
+    __syncthreads();
+    for (int st = 0; st < nsteps; ++st) {
+        const bool more = st + 1 < nsteps;
+        if (more) {
+            av = *reinterpret_cast<const u32x4 *>(asrc + (st + 1) * kStepK);
+            fetch(st + 1, nxt);
+        }
+        compute(st & 1, cur);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (more) {
+            stage_a(st + 1, (st + 1) & 1, av);
+            cur = nxt;
+        }
+        __syncthreads();
+    }
+
+    // Bias part: B' = biases of groups 32 c + 8 kq .. + 7 of the lane's
+    // column, A' = the group sums of row n over the same groups (0 past the
+    // last group), as fp16 hi + lo.
+    for (int c = 0; c * 32 < ngroups; ++c) {
+        h8 xh, xl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int g = 32 * c + 8 * kq + j;
+            const float v = g < ngroups ? sX[nl * ngroups + g] : 0.0f;
+            const f16 h = (f16)v;
+            xh[j] = h;
+            xl[j] = (f16)(v - (float)h);
+        }
+#pragma unroll
+        for (int cb = 0; cb < kNcb; ++cb) {
+            h8 bb;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int g = 32 * c + 8 * kq + j;
+                const uint16_t bv = ld16(br[mat(cb)], sb_index(col[cb], (uint32_t)min(g, ngroups - 1), ngroups) * 2);
+                bb[j] = g < ngroups ? __builtin_bit_cast(f16, bv) : (f16)0.0f;
+            }
+            tot[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, bb, tot[cb], 0, 0, 0);
+            tot[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, bb, tot[cb], 0, 0, 0);
+        }
+    }
+
+    // Epilogue: lane holds rows 4 kq + i of column col[cb].
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 4 * kq + i;
+        if (m >= m_end) continue;
+        if (GATEUP) {
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                const float gv = tot[cb][i], uv = tot[cb + 2][i];
+                const float hv = gv * __builtin_amdgcn_rcpf(1.0f + expf(-gv)) * uv;
+                a.H[(int64_t)m * a.f + col[cb]] = __builtin_bit_cast(uint16_t, (f16)hv);
+            }
+        } else {
+            const int p = a.perm[m];
+            const float wp = a.wsort[m];
+#pragma unroll
+            for (int cb = 0; cb < kNcb; ++cb) a.Yb[(int64_t)p * a.d + col[cb]] = wp * tot[cb][i];
+        }
+    }
+}
+
 template <int NB, bool GATEUP>
 __global__ __launch_bounds__(kGemmThreads, 2) void prefill_gemm_kernel(PrefillArgs a) {
     static_assert(!GATEUP || NB == 2, "gate/up runs two B operands per wave");
@@ -484,8 +703,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void prefill_gemm_kernel(PrefillAr
         prefill_tile<NB, GATEUP, 4>(a, s_a, e, m0, m_end, nt);
     else if (rows > 32)
         prefill_tile<NB, GATEUP, 2>(a, s_a, e, m0, m_end, nt);
-    else
+    else if (rows > 16 || (GATEUP ? a.d : a.f) / kGroup > kSmallMaxGroups)
         prefill_tile<NB, GATEUP, 1>(a, s_a, e, m0, m_end, nt);
+    else
+        prefill_small_tile<NB, GATEUP>(a, s_a, e, m0, m_end, nt);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,8 +1,10 @@
 """GPU parity: sorted whole-layer prefill (sort by expert, MFMA grouped GEMM,
 weighted combine) against the fp64 oracle, rel-L2 <= 1e-3 and, per token,
 max |y - ref| <= ELEM * max |ref|. fp16 MFMA operands (x exact; weights and
-the SwiGLU hidden rounded to fp16, each within 2^-11 relative) put the
-expected rel-L2 near 4e-4; the largest element error of a row is then about
+the SwiGLU hidden rounded to fp16, each within 2^-11 relative; tiles of at
+most 16 rows take the codes as exact fp16 denormals with scale and bias
+applied in fp32, so only the hidden is rounded there) put the expected
+rel-L2 near 4e-4; the largest element error of a row is then about
 as large relative to the row's largest value, and ELEM = 3e-3 leaves a
 margin while a wrong 32-row block or column block (an O(1) error on a few
 elements) still fails."""
@@ -86,6 +88,29 @@ def test_prefill_one_expert_takes_every_token():
     assert err == 0
     tok = np.arange(0, cfg.B, 13)
     U.assert_close(y[tok], _oracle(cfg, 0, x, idx, w, tok), TOL, ELEM)
+
+
+@pytest.mark.parametrize("d,f", [(4096, 256), (2176, 384)])
+def test_prefill_tails_at_the_small_tile_bound(d, f):
+    # Expert row counts chosen around the 16-row bound of the matrix-core
+    # path for small tiles: 1, 2 (tail of 130), 16 on it; 17, 20, 30, 86 on
+    # the 32-row blocks. d = 4096 gives 64 groups (two 32-group bias
+    # products); d = 2176 gives 34 (a partial second one) and a d_model that
+    # is not a multiple of 256 (down in 128-column blocks); the down
+    # reductions (4 and 6 groups) fill part of one bias product. Every token.
+    cfg = W.scaled(W.TINY, d=d, f=f, E=8, K=2, B=150)
+    store = U.gpu_store(cfg, [0])[0]
+    x = W.activations(cfg, 5, 0)
+    t = np.arange(cfg.B)
+    idx = np.stack([np.where(t < 130, 3, 5),
+                    np.select([t < 16, t < 33, t == 33, t < 120], [0, 1, 2, 4], 6)], axis=1).astype(np.int32)
+    assert sorted(np.bincount(idx.ravel(), minlength=cfg.E).tolist()) == [0, 1, 16, 17, 20, 30, 86, 130]
+    w = (0.1 + 0.9 * gen.uniform24(gen.draws(gen.stream_key(cfg.seed, gen.TAG_LOGITS, 99), cfg.B * cfg.K)))
+    w = w.reshape(cfg.B, cfg.K)
+    y, err = _prefill(cfg, store, x, idx, w)
+    assert err == 0
+    r, e = U.assert_close(y, _oracle(cfg, 0, x, idx, w, t), TOL, ELEM, f"small-tile bound d={d} f={f}")
+    print(f"small-tile bound d={d} f={f}: rel-L2 {r:.3g}, largest element error / row max {e:.3g}")
 
 
 def test_prefill_bad_ids_flag_and_skip():
