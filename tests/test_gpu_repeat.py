@@ -1,0 +1,94 @@
+"""Repeated calls on the same inputs give the same bytes. The prefill's sort
+and the batched decode's per-layer sort count pairs with LDS atomics, so the
+order of an expert's rows can differ from run to run; no output depends on
+it (each row is computed on its own, and sums run in k or expert order).
+Each call runs twice with its workspace filled with 0xFF bytes before each
+run, and the outputs are compared bit for bit."""
+import numpy as np
+import pytest
+
+import oracle
+from e0inputs import gen, workloads as W
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+def E():
+    from int4_gather_swiglu_amd import _lib
+    return _lib
+
+
+def _same_bytes(a, b, what):
+    assert a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8)), what
+
+
+@pytest.mark.parametrize("cfg", [W.scaled(W.TINY, B=300),
+                                 W.scaled(W.PREFILL35, B=1024, E=32)], ids=["tiny", "d2048_zipf"])
+def test_prefill_twice_same_bytes(cfg):
+    T = cfg.B
+    store = U.gpu_store(cfg, [0])[0]
+    x = W.activations(cfg, 7, 0)
+    idx, w = oracle.softmax_topk(W.given_logits(cfg, 7, 0).astype(np.float32), cfg.K)
+    counts = np.bincount(idx.ravel(), minlength=cfg.E)
+    bb = gen.bundle_bytes(cfg.d, cfg.f)
+    dims = E().moe_dims(cfg.d, cfg.f, cfg.E, cfg.K)
+    st = E().stack_from_bundles(store, cfg.d, cfg.f, bb, 0)
+    ws = U.empty((E().workspace_bytes(E().E0_OP_SORTED_PREFILL, dims, T),), "uint8")
+    xd, idd, wd = U.f16(x), U.i32(idx), U.f32(w.astype(np.float32))
+    outs = []
+    for _ in range(2):
+        ws.fill_(255)
+        y = U.empty((T, cfg.d))
+        err = U.zeros((1,), "int32")
+        E().e0_moe_sorted_prefill(dims, T, xd, idd, wd, st, y, ws, err)
+        U.torch().cuda.synchronize()
+        assert int(err.item()) == 0
+        outs.append(y.cpu().numpy())
+    print(f"prefill {cfg.name} T={T}: largest expert {counts.max()} rows, {int((counts > 0).sum())} active")
+    _same_bytes(outs[0], outs[1], "prefill y")
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_staged_decode_twice_same_bytes(B):
+    # The 8B tier's expert shape, every expert resident (slot = expert id):
+    # B = 1 runs the single-launch kernel, B = 8 the sorted batched kernels.
+    cfg = W.scaled(W.DECODE8_B32, L=1, B=B, K=4, E=16)
+    d, f, Ex, K = cfg.d, cfg.f, cfg.E, cfg.K
+    bb = gen.bundle_bytes(d, f)
+    pool = U.gpu_store(cfg, [0])
+    so = np.arange(Ex, dtype=np.int32)
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.choice(Ex, size=K, replace=False) for _ in range(B)]).astype(np.int32)
+    w = rng.uniform(0.1, 0.9, size=idx.shape).astype(np.float32)
+    x = W.activations(cfg, 3, 0)
+    dims = E().moe_dims(d, f, Ex, K)
+    ws = U.empty((E().workspace_bytes(E().E0_OP_STAGED_DECODE, dims, 1, B, 0),), "uint8")
+    xd, idd, wd, sod = U.f16(x[None]), U.i32(idx[None]), U.f32(w[None]), U.i32(so[None])
+    pst = E().stack_from_bundles(pool, d, f, bb, Ex * bb)
+    outs = []
+    for _ in range(2):
+        ws.fill_(255)
+        y = U.empty((1, B, d))
+        err = U.zeros((1,), "int32")
+        E().e0_moe_staged_decode(dims, 1, B, xd, idd, wd, sod, Ex, pst, None, y, ws, err)
+        U.torch().cuda.synchronize()
+        assert int(err.item()) == 0
+        outs.append(y.cpu().numpy())
+    _same_bytes(outs[0], outs[1], f"staged decode y, B={B}")
+
+
+def test_route_twice_same_bytes():
+    cfg = W.scaled(W.PREFILL35, B=300)
+    lg = W.given_logits(cfg, 2, 0)
+    p = E().route_params(0, cfg.K)
+    lgd = U.f16(lg[None])
+    outs = []
+    for _ in range(2):
+        idx = U.empty((1, cfg.B, cfg.K), "int32")
+        w = U.empty((1, cfg.B, cfg.K))
+        E().e0_route(p, 1, cfg.B, cfg.E, lgd, True, None, None, 0, idx, w, None)
+        U.torch().cuda.synchronize()
+        outs.append((idx.cpu().numpy(), w.cpu().numpy()))
+    _same_bytes(outs[0][0], outs[1][0], "route ids")
+    _same_bytes(outs[0][1], outs[1][1], "route weights")
