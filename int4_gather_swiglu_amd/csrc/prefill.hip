@@ -19,13 +19,13 @@
 //  3. gemm2    (tiles x d_model/256): Yb[pair] = w_pair * (H D^T).
 //  4. combine  : y[t] = sum over k in order of Yb[t*K + k].
 // The last M-tile of an expert runs only the 32-row MFMA blocks that hold
-// rows; a tile of at most 16 rows (the popularity tail) runs its own path.
+// rows; an expert with at most 16 rows (the popularity tail) runs its own path.
 // Tiles are dealt to the eight XCDs, heaviest first.
 //
 // MFMA v_mfma_f32_32x32x16_f16 on fp16 operands. A rows go from global memory
 // straight into LDS; B fragments are code words dequantised in registers (one
 // fp16 fma per weight, a single rounding of the exact dequantised value).
-// Tiles of at most 16 rows: v_mfma_f32_16x16x32_f16 with the code words as
+// Experts of at most 16 rows: v_mfma_f32_16x16x32_f16 with the code words as
 // exact fp16 denormals, the group scale applied to the products in fp32 and
 // the bias as a product of the rows' group sums with the biases.
 #include "e0_internal.h"
@@ -168,7 +168,8 @@ __global__ __launch_bounds__(kSortThreads) void prefill_sort_kernel(PrefillArgs 
     __syncthreads();
     // Scatter. The order of rows inside an expert's block follows the LDS
     // atomics and may differ from run to run; no output depends on it (every
-    // GEMM row is computed on its own and results are stored by pair index).
+    // GEMM row is computed on its own, with the same arithmetic in whichever
+    // of its expert's tiles it falls, and results are stored by pair index).
     for (int base = 0; base < n; base += kSortThreads * kSortBatch) {
         int ids[kSortBatch];
         float wts[kSortBatch];
@@ -456,9 +457,13 @@ E0_DEV void prefill_tile(const PrefillArgs &a, uint16_t (*s_a)[kTM * kARow], int
 }
 
 // ---------------------------------------------------------------------------
-// Tiles of at most 16 rows: most active experts of a layer receive only a
-// few of its pairs (the popularity tail), and a 32-row block would compute
-// padding while every weight of the tile is still dequantised. Here the
+// Experts with at most 16 rows (one tile): most active experts of a layer
+// receive only a few of its pairs (the popularity tail), and a 32-row block
+// would compute padding while every weight of the tile is still dequantised.
+// Only whole experts take this path: the sort orders an expert's rows by its
+// LDS atomics, so which rows fall in the tail tile of a larger expert can
+// change from run to run, and a row must get the same arithmetic whichever
+// tile holds it (every output is then the same from run to run). Here the
 // matrix cores take v_mfma_f32_16x16x32_f16 with the code words themselves
 // as the B operand, fp16 denormals q 2^-24 (exact), so no weight is
 // dequantised: the two MFMAs of quantisation group g give P_g = 2^-24
@@ -703,7 +708,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void prefill_gemm_kernel(PrefillAr
         prefill_tile<NB, GATEUP, 4>(a, s_a, e, m0, m_end, nt);
     else if (rows > 32)
         prefill_tile<NB, GATEUP, 2>(a, s_a, e, m0, m_end, nt);
-    else if (rows > 16 || (GATEUP ? a.d : a.f) / kGroup > kSmallMaxGroups)
+    else if (rows > 16 || m0 != a.off[e] || (GATEUP ? a.d : a.f) / kGroup > kSmallMaxGroups)
         prefill_tile<NB, GATEUP, 1>(a, s_a, e, m0, m_end, nt);
     else
         prefill_small_tile<NB, GATEUP>(a, s_a, e, m0, m_end, nt);

@@ -1,8 +1,8 @@
 """GPU parity: sorted whole-layer prefill (sort by expert, MFMA grouped GEMM,
 weighted combine) against the fp64 oracle, rel-L2 <= 1e-3 and, per token,
 max |y - ref| <= ELEM * max |ref|. fp16 MFMA operands (x exact; weights and
-the SwiGLU hidden rounded to fp16, each within 2^-11 relative; tiles of at
-most 16 rows take the codes as exact fp16 denormals with scale and bias
+the SwiGLU hidden rounded to fp16, each within 2^-11 relative; experts of
+at most 16 rows take the codes as exact fp16 denormals with scale and bias
 applied in fp32, so only the hidden is rounded there) put the expected
 rel-L2 near 4e-4; the largest element error of a row is then about
 as large relative to the row's largest value, and ELEM = 3e-3 leaves a
@@ -93,8 +93,9 @@ def test_prefill_one_expert_takes_every_token():
 @pytest.mark.parametrize("d,f", [(4096, 256), (2176, 384)])
 def test_prefill_tails_at_the_small_tile_bound(d, f):
     # Expert row counts chosen around the 16-row bound of the matrix-core
-    # path for small tiles: 1, 2 (tail of 130), 16 on it; 17, 20, 30, 86 on
-    # the 32-row blocks. d = 4096 gives 64 groups (two 32-group bias
+    # path for small experts: 1 and 16 on it; 2 (the tail of 130: a tail of a
+    # larger expert stays on the 32-row blocks), 17, 20, 30, 86 on the 32-row
+    # blocks. d = 4096 gives 64 groups (two 32-group bias
     # products); d = 2176 gives 34 (a partial second one) and a d_model that
     # is not a multiple of 256 (down in 128-column blocks); the down
     # reductions (4 and 6 groups) fill part of one bias product. Every token.
