@@ -1,7 +1,9 @@
 """Repeated calls on the same inputs give the same bytes. The prefill's sort
 and the batched decode's per-layer sort count pairs with LDS atomics, so the
 order of an expert's rows can differ from run to run; no output depends on
-it (each row is computed on its own, and sums run in k or expert order).
+it (each row is computed on its own, and sums run in k or expert order). The
+chained decode hands layers between workgroups through flags in its
+workspace; the prerouter routes its own logits.
 Each call runs twice with its workspace filled with 0xFF bytes before each
 run, and the outputs are compared bit for bit."""
 import numpy as np
@@ -49,10 +51,11 @@ def test_prefill_twice_same_bytes(cfg):
     _same_bytes(outs[0], outs[1], "prefill y")
 
 
-@pytest.mark.parametrize("B", [1, 8])
+@pytest.mark.parametrize("B", [1, 8, 32])
 def test_staged_decode_twice_same_bytes(B):
     # The 8B tier's expert shape, every expert resident (slot = expert id):
-    # B = 1 runs the single-launch kernel, B = 8 the sorted batched kernels.
+    # B = 1 runs the single-launch kernel, B = 8 and 32 the sorted batched
+    # kernels (at B = 32 about 8 tokens per expert: gate/up chunks of 4).
     cfg = W.scaled(W.DECODE8_B32, L=1, B=B, K=4, E=16)
     d, f, Ex, K = cfg.d, cfg.f, cfg.E, cfg.K
     bb = gen.bundle_bytes(d, f)
@@ -92,3 +95,59 @@ def test_route_twice_same_bytes():
         outs.append((idx.cpu().numpy(), w.cpu().numpy()))
     _same_bytes(outs[0][0], outs[1][0], "route ids")
     _same_bytes(outs[0][1], outs[1][1], "route weights")
+
+
+def test_chained_decode_twice_same_bytes():
+    # One token through 4 stacked layers in one launch (in-launch hand-offs
+    # between workgroups through flags in the workspace).
+    cfg = W.scaled(W.CHAIN35, E=24, L=4)
+    L = cfg.L
+    store = U.gpu_store(cfg, range(L))
+    bb = gen.bundle_bytes(cfg.d, cfg.f)
+    st = E().stack_from_bundles(store, cfg.d, cfg.f, bb, cfg.E * bb)
+    slot_of = U.i32(np.tile(np.arange(cfg.E, dtype=np.int32), (L, 1)))
+    lg = np.stack([W.given_logits(cfg, 0, l)[0] for l in range(L)]).astype(np.float32)
+    idx, w = oracle.softmax_topk(lg, cfg.K)
+    r0 = U.f32(W.residual0(cfg, 0))
+    g = U.f16(np.stack([W.norm_weight(cfg, l) for l in range(L)]))
+    idd, wd = U.i32(idx.astype(np.int32)), U.f32(w.astype(np.float32))
+    dims = E().moe_dims(cfg.d, cfg.f, cfg.E, cfg.K)
+    ws = U.empty((E().workspace_bytes(E().E0_OP_CHAINED_DECODE, dims, L, 0, 0),), "uint8")
+    outs = []
+    for _ in range(2):
+        ws.fill_(255)
+        y, r = U.empty((L, cfg.d)), U.empty((L, cfg.d))
+        err = U.zeros((1,), "int32")
+        E().e0_moe_chained_decode(dims, L, r0, g, 1e-6, idd, wd, slot_of, cfg.E, st, y, r, ws, err)
+        U.torch().cuda.synchronize()
+        assert int(err.item()) == 0
+        outs.append((y.cpu().numpy(), r.cpu().numpy()))
+    _same_bytes(outs[0][0], outs[1][0], "chained decode y")
+    _same_bytes(outs[0][1], outs[1][1], "chained decode residual")
+
+
+def test_prerouter_twice_same_bytes():
+    # All 32 heads of the prerouted 35B tier at one token: ids, weights and logits.
+    cfg = W.PREROUTED35
+    H, K, Ex, d = cfg.L, cfg.K, cfg.E, cfg.d
+    heads = [W.head(cfg, j) for j in range(H)]
+    st = lambda arrs: U.f16(np.stack(arrs))
+    hd = E().heads_from_tensors(st([h.fc1_w for h in heads]), st([h.fc1_b for h in heads]),
+                                st([h.fc2_w for h in heads]), st([h.fc2_b for h in heads]),
+                                st([h.lin_w for h in heads]))
+    rng = np.random.default_rng(9)
+    h = U.f16(gen.normal_f16(gen.stream_key(cfg.seed, gen.TAG_ACT, 77), H * d).reshape(H, 1, d))
+    cur = U.i32(np.stack([rng.choice(Ex, size=K, replace=False) for _ in range(H)]).reshape(H, 1, K).astype(np.int32))
+    prev = U.i32(np.stack([rng.choice(Ex, size=K, replace=False) for _ in range(H)]).reshape(H, 1, K).astype(np.int32))
+    dims = E().moe_dims(d, heads[0].fc1_w.shape[0], Ex, K)
+    ws = U.empty((E().workspace_bytes(E().E0_OP_PREROUTER, dims, H, 1, 0),), "uint8")
+    p = E().route_params(0, K)
+    outs = []
+    for _ in range(2):
+        ws.fill_(255)
+        idx, w, lo = U.empty((H, 1, K), "int32"), U.empty((H, 1, K)), U.empty((H, 1, Ex))
+        E().e0_prerouter(hd, H, 1, d, Ex, h, cur, prev, p, idx, w, lo, ws)
+        U.torch().cuda.synchronize()
+        outs.append((idx.cpu().numpy(), w.cpu().numpy(), lo.cpu().numpy()))
+    for i, what in enumerate(("ids", "weights", "logits")):
+        _same_bytes(outs[0][i], outs[1][i], f"prerouter {what}")
