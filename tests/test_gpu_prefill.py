@@ -114,6 +114,21 @@ def test_prefill_tails_at_the_small_tile_bound(d, f):
     print(f"small-tile bound d={d} f={f}: rel-L2 {r:.3g}, largest element error / row max {e:.3g}")
 
 
+@pytest.mark.parametrize("E,K,T", [(1024, 8, 200), (64, 1, 500), (16, 16, 40)])
+def test_prefill_routing_width_extremes(E, K, T):
+    # The widest expert count the call takes (1024: the sort's counters per
+    # thread), one expert per token, and every expert for every token (K = E).
+    cfg = W.scaled(W.TINY, E=E, K=K, B=T)
+    store = U.gpu_store(cfg, [0])[0]
+    x = W.activations(cfg, 6, 0)
+    idx, w = oracle.softmax_topk(W.given_logits(cfg, 6, 0).astype(np.float32), K)
+    w = w.astype(np.float32)
+    y, err = _prefill(cfg, store, x, idx, w)
+    assert err == 0
+    r, e = U.assert_close(y, _oracle(cfg, 0, x, idx, w, np.arange(T)), TOL, ELEM, f"E={E} K={K} T={T}")
+    print(f"E={E} K={K} T={T}: rel-L2 {r:.3g}, largest element error / row max {e:.3g}")
+
+
 def test_prefill_bad_ids_flag_and_skip():
     cfg = W.scaled(W.TINY, B=16)
     store = U.gpu_store(cfg, [0])[0]
