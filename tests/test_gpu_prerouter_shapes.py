@@ -1,10 +1,11 @@
 """GPU parity of e0_prerouter away from the prerouted tier's own shape: a
 d_model above 2048 (the general fc1 kernel: one wavefront per row, the hidden
-part streamed), several tokens per head, E = 128 with K = 8, and no previous
-token (prev_idx NULL: only the current K-hot columns). The logits are
-compared element by element with the oracle's fp64 head; the routed ids where
-the oracle's logits separate the K-th and (K+1)-th expert by more than the
-logits' error can move them, the weights within 1e-5."""
+part streamed), several tokens per head, E = 128 with K = 8, no previous
+token (prev_idx NULL: only the current K-hot columns), and the sigmoid-group
+rule (the 8B tier's routing) on the predicted logits. The logits are compared
+element by element with the oracle's fp64 head; the routed ids wherever the
+oracle's selection margin on its logits exceeds what the logits' error can
+move, the weights within 1e-5."""
 import numpy as np
 import pytest
 
@@ -22,10 +23,11 @@ def E():
     return _lib
 
 
-@pytest.mark.parametrize("d,Ex,K,B,with_prev", [(4096, 128, 8, 3, True), (2048, 256, 4, 5, False),
-                                                 (8192, 64, 2, 2, True)])
-def test_prerouter_shapes(d, Ex, K, B, with_prev):
-    cfg = W.scaled(W.PREROUTED35, d=d, E=Ex, K=K, L=3)
+@pytest.mark.parametrize("d,Ex,K,B,with_prev,mode", [(4096, 128, 8, 3, True, 0), (2048, 256, 4, 5, False, 0),
+                                                      (8192, 64, 2, 2, True, 0), (2048, 128, 8, 4, True, 1)])
+def test_prerouter_shapes(d, Ex, K, B, with_prev, mode):
+    grp = dict(mode=1, n_groups=8, topk_groups=4, scale=2.5) if mode else {}
+    cfg = W.scaled(W.PREROUTED35, d=d, E=Ex, K=K, L=3, **grp)
     H = cfg.L
     heads = [W.head(cfg, j) for j in range(H)]
     st = lambda arrs: U.f16(np.stack(arrs))
@@ -40,7 +42,7 @@ def test_prerouter_shapes(d, Ex, K, B, with_prev):
     ws = U.empty((E().workspace_bytes(E().E0_OP_PREROUTER, dims, H, B, 0),), "uint8")
     idx, w, lo = U.empty((H, B, K), "int32"), U.empty((H, B, K)), U.empty((H, B, Ex))
     E().e0_prerouter(hd, H, B, d, Ex, U.f16(h), U.i32(cur), U.i32(prev) if with_prev else None,
-                     E().route_params(0, K), idx, w, lo, ws)
+                     E().route_params(cfg.mode, K, cfg.n_groups, cfg.topk_groups, cfg.scale), idx, w, lo, ws)
     U.torch().cuda.synchronize()
     gi, gw, gl = idx.cpu().numpy(), w.cpu().numpy(), lo.cpu().numpy()
     worst, checked = 0.0, 0
@@ -49,12 +51,11 @@ def test_prerouter_shapes(d, Ex, K, B, with_prev):
             ref = oracle.head_logits(heads[j], h[j, b], cur[j, b], prev[j, b] if with_prev else None, K)
             worst = max(worst, float(np.abs(gl[j, b] - ref).max()))
             r32 = ref.astype(np.float32)[None]
-            srt = np.sort(ref)[::-1]
-            if srt[K - 1] - srt[K] > MARGIN:
-                ri, rw = oracle.softmax_topk(r32, K)
+            if oracle.route_margin(r32, cfg) > MARGIN:
+                ri, rw = oracle.route(r32, cfg)
                 assert np.array_equal(gi[j, b], ri[0]), (j, b)
                 assert np.abs(gw[j, b] - rw[0]).max() < 1e-5, (j, b)
                 checked += 1
-    print(f"d={d} E={Ex} K={K} B={B}: largest |logit - oracle| {worst:.3g}, ids checked on {checked}/{H * B} rows")
+    print(f"d={d} E={Ex} K={K} B={B} mode={mode}: largest |logit - oracle| {worst:.3g}, ids checked on {checked}/{H * B} rows")
     assert worst <= LOGIT_ATOL
     assert checked >= H * B // 2
