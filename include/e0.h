@@ -265,8 +265,12 @@ e0_status e0_moe_staged_decode_noalloc(const e0_moe_dims *dims, int32_t L, int32
  * discuss.pytorch.kr paths table: a layer's experts all resident, then a
  * sorted gather): the T*K (token, k) pairs are grouped by expert (the order
  * of the rows inside an expert's group is unspecified; no result depends on
- * it), each active expert runs as one grouped GEMM over its rows (matrix
- * cores), and the weighted results are summed back per token in k order:
+ * it: repeated calls on the same inputs give the same bytes), each active
+ * expert runs as one grouped GEMM over its rows (matrix cores; fp16 operands,
+ * the dequantised weight rounded to fp16 once, fp32 accumulation; an expert
+ * with at most 16 rows multiplies the codes themselves and applies its scales
+ * and biases in fp32), and the weighted results are summed back per token in
+ * k order:
  *   y[t] = sum_k w[t][k] * down(silu(gate(x_t)) * up(x_t)) of expert idx[t][k].
  *  x: device fp16 [T][d]; idx, w: device [T][K]; layer: slot e = expert e
  *  (layer_stride unused); y: device fp32 [T][d] (overwritten).
